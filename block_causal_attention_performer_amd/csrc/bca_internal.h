@@ -1,0 +1,85 @@
+// Internal declarations shared by the library's translation units (host
+// launchers and small device helpers).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bca.h"
+
+namespace bca {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKeyTile = 64;        // keys per attention tile (a tile never straddles a >=64 page)
+constexpr int kEulerTokens = 64;    // tokens per workgroup in the fused Euler kernel
+
+// ---------------------------------------------------------------- launchers
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_pages;
+  void* v_pages;
+  float* k_scales;
+  float* v_scales;
+  const int32_t* page_table;
+  int64_t n0;        // first logical position written
+  int64_t n_new;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t ps_log2;
+};
+hipError_t launch_append_copy(const AppendArgs& a, int elem_bytes, hipStream_t s);
+hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;
+  void* out;
+  const void* k_pages;
+  const void* v_pages;
+  const float* k_scales;
+  const float* v_scales;
+  const int32_t* page_table;
+  float* ws_o;       // split partials: [nsplit][n_q][H][D] fp32 (unnormalised)
+  float* ws_ml;      // [nsplit][n_q][H][2]  (running max in log2 units, row sum)
+  int64_t n_q;
+  int64_t q_pos0;
+  int64_t n_kv;
+  int32_t block_size;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t ps_log2;
+  int32_t nsplit;
+  int32_t out_f32;
+  float scale_log2;  // softmax_scale * log2(e)
+  float scale;       // softmax_scale
+};
+// bf16 / fp8 MFMA path.  kv_fp8 selects fp8 pages.  Returns the error of the
+// launch; nsplit > 1 also launches the combine.
+hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+// Query rows per attention workgroup (the unit of the split heuristic).
+int attn_mfma_rows_per_wg();
+
+struct EulerArgs {
+  float* z;
+  const void* x;
+  const float* w;
+  float* ws_part;    // [ksplit][n_tok][16] fp32
+  int32_t* counters; // [ceil(n_tok/64)], zero between calls
+  int64_t n_tok;
+  int32_t k;
+  int32_t n_ch;
+  int32_t ksplit;
+  int32_t kchunk;    // k per split (multiple of 32)
+  float dtau;
+};
+hipError_t launch_euler_bf16_proj(const EulerArgs& a, hipStream_t s);
+hipError_t launch_euler_generic(const EulerArgs& a, bool x_f32, hipStream_t s);
+hipError_t launch_euler_plain(const EulerArgs& a, hipStream_t s);
+
+}  // namespace bca

@@ -1,0 +1,64 @@
+"""fm_euler_step parity: closed-form interpolant with the exact velocity, and
+the fused velocity projection against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from _helpers import assert_close, np64, say
+
+pytestmark = pytest.mark.gpu
+bca = pytest.importorskip("block_causal_attention_performer_amd")
+
+
+def test_exact_velocity_reproduces_interpolant():
+    """tiny fp32 workload: z(1) = eps, v = eps - z0, 4 uniform steps; every
+    iterate is (1 - tau) z0 + tau eps and the last is z0."""
+    w = workloads.WORKLOADS["tiny_f32"]
+    eps = workloads.randn((w.unit_tokens, w.n_ch), workloads.seed_for(w.index, "eps"))
+    z0 = workloads.randn((w.unit_tokens, w.n_ch), workloads.seed_for(w.index, "z0"))
+    vel = (eps - z0).cuda()
+    z = eps.clone().cuda()
+    S = w.n_steps
+    want = oracle.euler_solve(eps.double().numpy(), lambda zz, t: (eps - z0).double().numpy(), S,
+                              record=True)[1]
+    for s in range(S):
+        bca.fm_euler_step(z, vel, None, 1.0 / S)
+        tau = 1.0 - (s + 1) / S
+        closed = (1 - tau) * z0.double().numpy() + tau * eps.double().numpy()
+        assert_close(np64(z), closed, 1e-4, what=f"step {s} closed form")
+        assert_close(np64(z), want[s + 1], 1e-4, what=f"step {s} oracle")
+    assert_close(np64(z), z0.double().numpy(), 1e-4, what="z(0) == z0")
+
+
+@pytest.mark.parametrize("n_tok,H,D", [(3712, 40, 128), (1024, 24, 128), (77, 4, 64), (5, 1, 64)])
+@pytest.mark.parametrize("with_ws", [True, False])
+def test_bf16_projection(n_tok, H, D, with_ws):
+    k = H * D
+    say(f"euler bf16 n_tok={n_tok} k={k} ws={with_ws}")
+    x = workloads.qkv(3, n_tok, H, D, 0.05, "bf16")
+    w = workloads.randn((k, 16), 4)
+    z = workloads.randn((n_tok, 16), 5)
+    zg = z.clone().cuda()
+    ws = None
+    if with_ws:
+        c = bca.KVCache(H, D, 256, torch.zeros(1, dtype=torch.int32), 1, "bf16")
+        ws = bca.alloc_workspace(bca.workspace_bytes(c, n_tok, n_tok))
+    for _ in range(2):      # twice: the split counters must come back to zero
+        bca.fm_euler_step(zg, x.cuda(), w.cuda(), 0.25, workspace=ws)
+    v = oracle.velocity(x.double().numpy(), w.double().numpy())
+    want = z.double().numpy() - 0.25 * v - 0.25 * v
+    # the projection is exact up to fp32 accumulation and W's 2^-16 split
+    assert_close(np64(zg), want, 1e-4, what="bf16 projection")
+
+
+def test_f32_projection_generic():
+    n_tok, k = 16, 256
+    x = workloads.randn((n_tok, k), 7, 0.1)
+    w = workloads.randn((k, 16), 8)
+    z = workloads.randn((n_tok, 16), 9)
+    zg = z.clone().cuda()
+    bca.fm_euler_step(zg, x.cuda(), w.cuda(), 0.25)
+    want = z.double().numpy() - 0.25 * oracle.velocity(x.double().numpy(), w.double().numpy())
+    assert_close(np64(zg), want, 1e-5, what="f32 projection")
