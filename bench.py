@@ -1,0 +1,250 @@
+"""Benchmark of the performer step on one MI355X.
+
+One step = one performer_unit at the v0.2 unit shapes: kv_append of a
+3712-token K/V slice (40 heads x 128, bf16) after 32 units of history
+(118,784 tokens, 256-token pages, shuffled physical pages), then 4 x
+(block_causal_attn over all 122,496 keys + fm_euler_step with the 5120x16
+projection).  The cache is rolled back to the history length before every
+step (host field only), so every step does the same work.
+
+Prints one JSON line.  value = attention FLOPs of the unit (4 calls x
+4*H*D*Lq*Nk) / wall time of the whole unit (append and Euler included).
+roofline = the attention kernel alone, timed with HIP events recorded on the
+launch stream around every attention call of the timed steps.
+cpu_baseline = the float64 CPU oracle on a bounded sample of the same
+attention (rank 0 only).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-causal attn TFLOP/s (% MFMA peak) + ms/160ms-unit at v0.2 shapes"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+UNIT_BUDGET_MS = 160.0
+ATTN_KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_performer_amd", "csrc", "attn_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_v02_unit_traffic.txt")
+
+
+class Hip:
+    """hipEvent_* through the HIP runtime (events on the launch stream)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.L.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+
+def _kernel_hash() -> str:
+    return hashlib.sha256(open(ATTN_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(flops_unit_bytes=None):
+    """HBM bytes per attention launch from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != _kernel_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, w, rows_n, heads_n):
+    """Time the float64 oracle on rows_n query rows x heads_n heads over the
+    whole key range (same inputs as the GPU step)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    H = w.n_heads
+    rows = np.linspace(0, w.unit_tokens - 1, rows_n).astype(np.int64)
+    heads = np.arange(0, H, max(1, H // heads_n))[:heads_n]
+    hsel = torch.as_tensor(heads, device=inp["q"].device)
+    q = inp["q"][:, hsel].float().cpu().numpy().astype(np.float64)
+    k = torch.cat([inp["k_hist"][:, hsel], inp["k_new"][:, hsel]]).float().cpu().numpy().astype(np.float64)
+    v = torch.cat([inp["v_hist"][:, hsel], inp["v_new"][:, hsel]]).float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.attention_dense(q, k, v, w.n_hist, w.unit_tokens, rows=rows)
+    del q, k, v
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * len(rows) * len(heads) * w.n_kv
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"attention_dense (float64 numpy) of {len(rows)} query rows x {len(heads)} "
+                      f"heads over all {w.n_kv} keys of the v0.2 unit; {dt:.2f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v02_unit")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (PMC calibration)")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    global torch
+    import torch
+    import block_causal_attention_performer_amd as bca
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    print(f"[bench] workload {w.name}: generating inputs on device", file=sys.stderr, flush=True)
+    inp = workloads.make_unit_inputs(w, device=dev)
+    H, D, ps, lq = w.n_heads, w.head_dim, w.page_size, w.unit_tokens
+    n_log = -(-w.n_kv // ps)
+    pt = workloads.page_table(n_log, n_log + 1, 1234)
+    cache = bca.KVCache(H, D, ps, pt, n_log + 1, w.dtype if w.dtype != "fp8" else "fp8", device=dev)
+    bca.kv_append(cache, inp["k_hist"], inp["v_hist"])
+    ws = bca.alloc_workspace(bca.workspace_bytes(cache, lq, w.n_kv, w.n_ch))
+    osc = torch.empty((lq, H, D), dtype=torch.bfloat16, device=dev)
+    z = inp["eps"].clone()
+    S = w.n_steps
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        cache.c.n_tokens = w.n_hist
+        z.copy_(inp["eps"])
+        bca.performer_unit(cache, inp["k_new"], inp["v_new"], inp["q"], inp["w"], z, S,
+                           o_scratch=osc, workspace=ws, attn_events=events)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(2 * S)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_unit = wall * 1e3 / args.steps
+    attn_ms = [hip.elapsed_ms(e[2 * s], e[2 * s + 1]) for e in evs for s in range(S)]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    flops_call = w.attn_flops()
+    attn_tflops = flops_call / (attn_avg * 1e-3) / 1e12
+    value = S * flops_call / (ms_unit * 1e-3) / 1e12
+
+    # ---- append and Euler alone (events around each call; caches flushed
+    # between reps by writing a 1 GiB buffer)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    e0, e1 = hip.event(), hip.event()
+    app_ms, eul_ms = [], []
+    for _ in range(args.kernel_reps):
+        flush.fill_(1)
+        cache.c.n_tokens = w.n_hist
+        hip.record(e0, stream)
+        bca.kv_append(cache, inp["k_new"], inp["v_new"])
+        hip.record(e1, stream)
+        app_ms.append(hip.elapsed_ms(e0, e1))
+        flush.fill_(2)
+        hip.record(e0, stream)
+        bca.fm_euler_step(z, osc, inp["w"], 1.0 / S, workspace=ws)
+        hip.record(e1, stream)
+        eul_ms.append(hip.elapsed_ms(e0, e1))
+    del flush
+    app_bytes = 2 * 2 * lq * H * D * 2            # read + write, K and V
+    eul_bytes = lq * H * D * 2 + H * D * 16 * 4 + 2 * lq * 16 * 4
+    app_med = sorted(app_ms)[len(app_ms) // 2]
+    eul_med = sorted(eul_ms)[len(eul_ms) // 2]
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_unit, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded device draws, 0.5*N(0,1) Q/K/V rounded to bf16)",
+        "config": {"workload": w.name, "heads": H, "head_dim": D, "unit_tokens": lq,
+                   "hist_tokens": w.n_hist, "n_kv": w.n_kv, "page_size": ps,
+                   "solver_steps": S, "latent_channels": w.n_ch, "parallelism": "none"},
+        "ms_per_unit": round(ms_unit, 4),
+        "units_per_s": round(1e3 / ms_unit, 2),
+        "unit_budget_frac": round(ms_unit / UNIT_BUDGET_MS, 4),
+        "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(), "kernel": "attn_mfma_kernel",
+                     "avg_launch_ms": round(attn_avg, 4), "flops_per_launch": flops_call},
+        "kernels": {
+            "kv_append": {"median_ms": round(app_med, 5), "bytes": app_bytes,
+                          "GBps": round(app_bytes / (app_med * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(app_bytes / (app_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "fm_euler_step": {"median_ms": round(eul_med, 5), "bytes": eul_bytes,
+                              "GBps": round(eul_bytes / (eul_med * 1e-3) / 1e9, 1),
+                              "hbm_frac": round(eul_bytes / (eul_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_rows, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,9 +94,16 @@ struct AttnPlan {
   size_t o_bytes;
 };
 
+// Attention workspace: overflow flags, then (with a split) the partials.
+size_t attn_flag_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
+  const int64_t BM = attn_mfma_rows_per_wg();
+  const int64_t nqt = (n_q + BM - 1) / BM;
+  return align256((size_t)nqt * c->n_heads * nsplit * kAttnFlagWaves * 4);
+}
 size_t attn_split_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
   const size_t per = (size_t)nsplit * n_q * c->n_heads;
-  return align256(per * c->head_dim * 4) + align256(per * 2 * 4);
+  const size_t parts = nsplit > 1 ? align256(per * c->head_dim * 4) + align256(per * 2 * 4) : 0;
+  return attn_flag_bytes(c, n_q, nsplit) + parts;
 }
 
 size_t euler_counter_bytes(int64_t n_tok) {
@@ -122,7 +129,7 @@ int choose_attn_split(const bca_kv_cache* c, int64_t n_q, int64_t q_pos0, int32_
   int best = 1;
   double best_cost = 1e300;
   for (int s = 1; s <= kMaxAttnSplit; ++s) {
-    if (s > 1 && attn_split_bytes(c, n_q, s) > room) break;
+    if (attn_split_bytes(c, n_q, s) > room) break;
     if (tiles / s < 4.0 && s > 1) break;
     const double rounds = ceil(wgs * s / cus);
     const double cost = rounds * (tiles / s + 6.0) + (s > 1 ? 2.0 + 0.5 * s : 0.0);
@@ -174,14 +181,35 @@ bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t bloc
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   const size_t room = workspace ? workspace_bytes : 0;
-  a.nsplit = choose_attn_split(c, n_q, q_pos0, block_size, n_kv, room);
-  if (a.nsplit > 1) {
-    const size_t per = (size_t)a.nsplit * n_q * c->n_heads;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(per * c->head_dim * 4));
+  const bool fp8 = c->dtype == BCA_FP8_E4M3;
+  hipError_t e;
+  if (c->dtype == BCA_F32) {
+    a.nsplit = 1;
+    e = launch_attn_f32(a, s);
+  } else if (room >= attn_split_bytes(c, n_q, 1)) {
+    // fast kernel (+ combine), then the exact kernel for flagged query tiles
+    a.nsplit = choose_attn_split(c, n_q, q_pos0, block_size, n_kv, room);
+    char* ws = static_cast<char*>(workspace);
+    a.flags_out = reinterpret_cast<int32_t*>(ws);
+    ws += attn_flag_bytes(c, n_q, a.nsplit);
+    if (a.nsplit > 1) {
+      const size_t per = (size_t)a.nsplit * n_q * c->n_heads;
+      a.ws_o = reinterpret_cast<float*>(ws);
+      a.ws_ml = reinterpret_cast<float*>(ws + align256(per * c->head_dim * 4));
+    }
+    e = launch_attn_mfma(a, fp8, s);
+    if (e == hipSuccess) {
+      AttnArgs x = a;
+      x.flags = a.flags_out;
+      x.flag_splits = a.nsplit;
+      x.flags_out = nullptr;
+      x.nsplit = 1;
+      e = launch_attn_exact(x, fp8, s);
+    }
+  } else {
+    a.nsplit = 1;
+    e = launch_attn_exact(a, fp8, s);
   }
-  hipError_t e = c->dtype == BCA_F32 ? launch_attn_f32(a, s)
-                                     : launch_attn_mfma(a, c->dtype == BCA_FP8_E4M3, s);
   return e == hipSuccess ? BCA_OK : BCA_EHIP;
 }
 

@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeyTile = 64;        // keys per attention tile (a tile never straddles a >=64 page)
 constexpr int kEulerTokens = 64;    // tokens per workgroup in the fused Euler kernel
+constexpr int kAttnFlagWaves = 8;   // overflow flags per (query tile, split) of the fast attention kernel
 
 // ---------------------------------------------------------------- launchers
 
@@ -45,7 +46,10 @@ struct AttnArgs {
   const float* v_scales;
   const int32_t* page_table;
   float* ws_o;       // split partials: [nsplit][n_q][H][D] fp32 (unnormalised)
-  float* ws_ml;      // [nsplit][n_q][H][2]  (running max in log2 units, row sum)
+  float* ws_ml;      // [nsplit][n_q][H][2]  (reference max in log2 units, row sum)
+  int32_t* flags_out;    // fast kernel: [H][n_qtiles][nsplit][kAttnFlagWaves] overflow flags
+  const int32_t* flags;  // exact kernel: recompute only query tiles flagged here
+  int32_t flag_splits;   // nsplit the flags were written with
   int64_t n_q;
   int64_t q_pos0;
   int64_t n_kv;
@@ -59,8 +63,11 @@ struct AttnArgs {
   float scale;       // softmax_scale
 };
 // bf16 / fp8 MFMA path.  kv_fp8 selects fp8 pages.  Returns the error of the
-// launch; nsplit > 1 also launches the combine.
+// launch; nsplit > 1 also launches the combine.  Needs flags_out.
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s);
+// Exact-rescaling MFMA kernel (no split); with flags set it only rewrites
+// flagged query tiles.
+hipError_t launch_attn_exact(const AttnArgs& a, bool kv_fp8, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 // Query rows per attention workgroup (the unit of the split heuristic).
 int attn_mfma_rows_per_wg();

@@ -81,7 +81,9 @@ def attention_dense(q, k, v, q_pos0: int = 0, block_size: Optional[int] = None,
     if block_size is None:
         mask = np.ones((len(rows), n_kv), dtype=bool)
     else:
-        mask = visibility_mask(n_q, q_pos0, n_kv, block_size)[rows]
+        # the rule of visibility_mask, evaluated for the selected rows only
+        qb = (q_pos0 + rows) // block_size
+        mask = (np.arange(n_kv) // block_size)[None, :] <= qb[:, None]
     out = np.zeros((len(rows), len(heads), D), dtype=np.float64)
     for a, h in enumerate(heads):
         s = (q[rows, h, :] @ k[:, h, :].T) * scale

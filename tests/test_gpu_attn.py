@@ -56,6 +56,12 @@ def test_tiny_f32_incremental(ps, shuffle):
     assert_close(got, want, F32_TOL, what="incremental f32")
 
 
+def _ws(g, n_q, n_kv, on):
+    """Workspace on: fast kernel (+ split, + exact rerun of flagged tiles);
+    off: the exact-rescaling kernel alone."""
+    return bca.alloc_workspace(bca.workspace_bytes(g, n_q, n_kv)) if on else None
+
+
 def _bf16_case(H, D, n_kv, ps, shuffle, seed, scale=1.0):
     q = workloads.qkv(seed, n_kv, H, D, scale, "bf16")
     k = workloads.qkv(seed + 1, n_kv, H, D, scale, "bf16")
@@ -68,14 +74,15 @@ def _bf16_case(H, D, n_kv, ps, shuffle, seed, scale=1.0):
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("ps,shuffle", [(256, None), (16, 4), (64, 9)])
 @pytest.mark.parametrize("n_kv,n_q", [(1000, 300), (4160, 777), (300, 300), (70, 5)])
-def test_bf16_streaming(D, ps, shuffle, n_kv, n_q):
+@pytest.mark.parametrize("ws", [False, True])
+def test_bf16_streaming(D, ps, shuffle, n_kv, n_q, ws):
     """The streaming call: the last n_q tokens form the current block and see
     every cached key; ragged key and query tails."""
     H = 3
-    say(f"bf16 streaming D={D} ps={ps} n_kv={n_kv} n_q={n_q}")
+    say(f"bf16 streaming D={D} ps={ps} n_kv={n_kv} n_q={n_q} ws={ws}")
     q, k, v, g, _ = _bf16_case(H, D, n_kv, ps, shuffle, 31)
     qq = q[n_kv - n_q:]
-    out = bca.block_causal_attn(qq.cuda(), g)
+    out = bca.block_causal_attn(qq.cuda(), g, workspace=_ws(g, n_q, n_kv, ws))
     want = oracle.attention_dense(qq.double().numpy(), k.double().numpy(), v.double().numpy(),
                                   n_kv - n_q, n_q)
     assert_close(np64(out), want, BF16_TOL, BF16_REL, what="streaming bf16")
@@ -83,18 +90,21 @@ def test_bf16_streaming(D, ps, shuffle, n_kv, n_q):
 
 @pytest.mark.parametrize("B", [1, 16, 100, 256, 1000])
 @pytest.mark.parametrize("ps", [256, 16])
-def test_bf16_multiblock(B, ps):
+@pytest.mark.parametrize("ws", [False, True])
+def test_bf16_multiblock(B, ps, ws):
     """Full-sequence prefill call with many blocks: masked diagonal tiles,
     skipped future tiles; block 1 is causal."""
     H, D, n = 2, 128, 900
-    say(f"bf16 multiblock B={B} ps={ps}")
+    say(f"bf16 multiblock B={B} ps={ps} ws={ws}")
     q, k, v, g, _ = _bf16_case(H, D, n, ps, 3, 57)
-    out = bca.block_causal_attn(q.cuda(), g, n_kv=n, q_pos0=0, block_size=B)
+    out = bca.block_causal_attn(q.cuda(), g, n_kv=n, q_pos0=0, block_size=B,
+                                workspace=_ws(g, n, n, ws))
     want = oracle.attention_dense(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0, B)
     assert_close(np64(out), want, BF16_TOL, BF16_REL, what=f"multiblock B={B}")
 
 
-def test_bf16_middle_unit_and_out_f32():
+@pytest.mark.parametrize("ws", [False, True])
+def test_bf16_middle_unit_and_out_f32(ws):
     """Queries of a middle unit (q_pos0 > 0, later keys present but hidden)
     with fp32 output."""
     H, D, n = 2, 128, 1500
@@ -102,7 +112,7 @@ def test_bf16_middle_unit_and_out_f32():
     q_pos0, n_q, B = 600, 300, 300
     qq = q[q_pos0:q_pos0 + n_q]
     out = bca.block_causal_attn(qq.cuda(), g, n_kv=n, q_pos0=q_pos0, block_size=B,
-                                out_dtype=torch.float32)
+                                out_dtype=torch.float32, workspace=_ws(g, n_q, n, ws))
     assert out.dtype == torch.float32
     want = oracle.attention_dense(qq.double().numpy(), k[:900].double().numpy(),
                                   v[:900].double().numpy(), 600, B)
@@ -127,7 +137,8 @@ def test_split_kv_matches_single_pass():
     assert torch.equal(b, c)
 
 
-def test_bitwise_invariants():
+@pytest.mark.parametrize("ws", [False, True])
+def test_bitwise_invariants(ws):
     """P5 shuffled page table, P7 garbage appended past n_kv, determinism."""
     H, D, n_kv, n_q = 3, 128, 2000, 333
     q = workloads.qkv(5, n_q, H, D, 1.0, "bf16").cuda()
@@ -137,20 +148,24 @@ def test_bitwise_invariants():
     for shuffle in (None, 12):
         g, _, _ = make_caches(bca, H, D, 256, "bf16", n_kv + 500, shuffle)
         bca.kv_append(g, k.cuda(), v.cuda())
-        outs.append(bca.block_causal_attn(q, g, n_kv=n_kv))
-        outs.append(bca.block_causal_attn(q, g, n_kv=n_kv))
+        w = _ws(g, n_q, n_kv, ws)
+        outs.append(bca.block_causal_attn(q, g, n_kv=n_kv, workspace=w))
+        outs.append(bca.block_causal_attn(q, g, n_kv=n_kv, workspace=w))
         junk = torch.full((500, H, D), float("nan"), dtype=torch.bfloat16)
         bca.kv_append(g, junk.cuda(), junk.cuda())
-        outs.append(bca.block_causal_attn(q, g, n_kv=n_kv))
+        outs.append(bca.block_causal_attn(q, g, n_kv=n_kv, workspace=w))
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
 
 
-def test_peaky_planted_keys():
+@pytest.mark.parametrize("ws", [False, True])
+def test_peaky_planted_keys(ws):
     """Sharp softmax: logits x16 and keys planted equal to chosen queries at
     the first page, a page boundary and inside the current block; a wrong page
-    or mask shows as an O(1) error."""
+    or mask shows as an O(1) error.  With a workspace the planted keys far
+    above the first tile's maximum send their query tiles through the
+    overflow flag to the exact kernel."""
     H, D, n_kv, n_q = 2, 128, 3000, 200
     q = workloads.qkv(41, n_q, H, D, 1.0, "bf16")
     k = workloads.qkv(42, n_kv, H, D, 1.0, "bf16")
@@ -160,7 +175,7 @@ def test_peaky_planted_keys():
     g, _, _ = make_caches(bca, H, D, 256, "bf16", n_kv, 8)
     bca.kv_append(g, k.cuda(), v.cuda())
     scale = 4.0 / np.sqrt(D)
-    out = bca.block_causal_attn(q.cuda(), g, softmax_scale=scale)
+    out = bca.block_causal_attn(q.cuda(), g, softmax_scale=scale, workspace=_ws(g, n_q, n_kv, ws))
     want = oracle.attention_dense(q.double().numpy(), k.double().numpy(), v.double().numpy(),
                                   n_kv - n_q, n_q, scale=scale)
     assert_close(np64(out), want, BF16_TOL, BF16_REL, what="peaky")

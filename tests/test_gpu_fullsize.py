@@ -1,0 +1,103 @@
+"""Parity at the full v0.2 sizes, in the launch configuration bench.py times
+(workspace given: split key range, fast kernel + exact rerun of flagged
+tiles).  Inputs are the seeded device draws of workloads.make_unit_inputs;
+the oracle evaluates sampled query rows (all heads) over the whole cache in
+float64, head by head."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from _helpers import assert_close, say
+
+pytestmark = pytest.mark.gpu
+bca = pytest.importorskip("block_causal_attention_performer_amd")
+
+ROWS = np.array([0, 1, 31, 32, 255, 256, 1000, 1855, 2047, 3000, 3583, 3584, 3700, 3711])
+
+
+def _setup(name, qk_factor=1.0, plant=None):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_unit_inputs(w, device="cuda")
+    if qk_factor != 1.0:
+        for key in ("q", "k_hist", "k_new"):
+            inp[key] = workloads.peaky(inp[key], qk_factor)
+    if plant:
+        k_all_idx = []
+        for qi, kj in plant:
+            if kj < w.n_hist:
+                inp["k_hist"][kj] = inp["q"][qi]
+            else:
+                inp["k_new"][kj - w.n_hist] = inp["q"][qi]
+            k_all_idx.append(kj)
+    H, D, ps = w.n_heads, w.head_dim, w.page_size
+    n_log = -(-w.n_kv // ps)
+    pt = workloads.page_table(n_log, n_log + 1, 1234)
+    g = bca.KVCache(H, D, ps, pt, n_log + 1, "bf16")
+    bca.kv_append(g, inp["k_hist"], inp["v_hist"])
+    ws = bca.alloc_workspace(bca.workspace_bytes(g, w.unit_tokens, w.n_kv, w.n_ch))
+    return w, inp, g, ws
+
+
+def _oracle_rows(w, inp, rows, scale=None):
+    """attention of the sampled rows over all keys, per head, float64."""
+    H, D = w.n_heads, w.head_dim
+    out = np.zeros((len(rows), H, D))
+    q = inp["q"][rows.tolist()].float().cpu().numpy().astype(np.float64)
+    for h in range(H):
+        k = torch.cat([inp["k_hist"][:, h], inp["k_new"][:, h]]).float().cpu().numpy().astype(np.float64)
+        v = torch.cat([inp["v_hist"][:, h], inp["v_new"][:, h]]).float().cpu().numpy().astype(np.float64)
+        qq = q[:, h:h + 1, :]
+        out[:, h:h + 1, :] = oracle.attention_dense(qq, k[:, None, :], v[:, None, :], scale=scale)
+    return out
+
+
+def test_v02_attention_sampled_rows():
+    """One streaming block_causal_attn call at the v0.2 unit (40 x 128, 3712
+    queries over 122,496 keys in 256-token pages)."""
+    say("v0.2 attention full size")
+    w, inp, g, ws = _setup("v02_attn")
+    bca.kv_append(g, inp["k_new"], inp["v_new"])
+    out = bca.block_causal_attn(inp["q"], g, workspace=ws)
+    again = bca.block_causal_attn(inp["q"], g, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    want = _oracle_rows(w, inp, ROWS)
+    got = out[ROWS.tolist()].float().cpu().numpy()
+    assert_close(got, want, 2e-2, 1e-2, what="v0.2 O sampled rows")
+
+
+def test_v02_attention_peaky_planted():
+    """Sharp-softmax v0.2 variant: Q and K x4 (logit std ~4) and keys equal
+    to chosen queries planted in the first page, at a page boundary, deep in
+    the history and inside the current block."""
+    say("v0.2 attention peaky")
+    plant = [(0, 5), (1, 255), (256, 256), (1000, 60000), (3583, 118784 + 100), (3711, 122495)]
+    w, inp, g, ws = _setup("v02_attn", qk_factor=4.0, plant=plant)
+    bca.kv_append(g, inp["k_new"], inp["v_new"])
+    out = bca.block_causal_attn(inp["q"], g, workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set([r for r, _ in plant] + [2, 3000])))
+    want = _oracle_rows(w, inp, rows)
+    got = out[rows.tolist()].float().cpu().numpy()
+    assert_close(got, want, 2e-2, 1e-2, what="v0.2 peaky O")
+
+
+def test_v02_performer_unit_sampled_rows():
+    """The full v0.2 performer unit (append + 4 x (attention + Euler) with the
+    5120 x 16 projection), exactly as bench.py runs it."""
+    say("v0.2 performer unit full size")
+    w, inp, g, ws = _setup("v02_unit")
+    z = inp["eps"].clone()
+    osc = torch.empty((w.unit_tokens, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    bca.performer_unit(g, inp["k_new"], inp["v_new"], inp["q"], inp["w"], z, w.n_steps,
+                       o_scratch=osc, workspace=ws)
+    torch.cuda.synchronize()
+    assert g.n_tokens == w.n_kv
+    o_want = _oracle_rows(w, inp, ROWS)
+    v = oracle.velocity(o_want, inp["w"].double().cpu().numpy())
+    eps = inp["eps"][ROWS.tolist()].double().cpu().numpy()
+    z_want = oracle.euler_solve(eps, lambda zz, tau: v, w.n_steps)
+    assert_close(osc[ROWS.tolist()].float().cpu().numpy(), o_want, 2e-2, 1e-2, what="v0.2 unit O")
+    assert_close(z[ROWS.tolist()].cpu().numpy(), z_want, 2e-2, 1e-2, what="v0.2 unit z")

@@ -45,7 +45,7 @@ def _run(H, D, lq, hist_units, ps, dtype, shuffle, qkv_scale, seed, rows=None, w
 @pytest.mark.parametrize("ps,shuffle", [(256, None), (16, 6)])
 def test_small_unit(dtype, D, tol_o, tol_z, ps, shuffle):
     say(f"performer small dtype={dtype} ps={ps}")
-    zg, og, zw, ow = _run(4, D, 48, 5, ps, dtype, shuffle, 1.0, 60)
+    zg, og, zw, ow = _run(4, D, 48, 5, ps, dtype, shuffle, 0.5, 60)
     assert_close(og, ow, tol_o, 1e-2 if dtype == "bf16" else None, what="O")
     assert_close(zg, zw, tol_z, what="z")
 
