@@ -119,8 +119,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v02_unit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=128)
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (PMC calibration)")
     ap.add_argument("--kernel-reps", type=int, default=20)

@@ -159,8 +159,9 @@ def workspace_bytes(cache: KVCache, n_q: int, n_kv: int, n_ch: int = 16) -> int:
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace, as fm_euler_step requires before first use."""
-    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """Device workspace of at least nbytes (the kernels need no particular
+    initial contents)."""
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def kv_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:

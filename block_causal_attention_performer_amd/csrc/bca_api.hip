@@ -13,8 +13,6 @@ using namespace bca;
 namespace {
 
 constexpr int kMaxAttnSplit = 8;
-constexpr int kMaxEulerSplit = 64;
-constexpr int kEulerMaxChunk = 640;
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int64_t x) { int l = 0; while ((int64_t{1} << l) < x) ++l; return l; }
@@ -106,9 +104,9 @@ size_t attn_split_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
   return attn_flag_bytes(c, n_q, nsplit) + parts;
 }
 
-size_t euler_counter_bytes(int64_t n_tok) {
-  return align256((size_t)((n_tok + kEulerTokens - 1) / kEulerTokens) * 4);
-}
+// Workspace layout: [W transposed to bf16 hi/lo, 64 bytes per row of W]
+// [attention: overflow flags, split partials].
+size_t euler_wt_bytes(int64_t k) { return align256((size_t)k * 16 * 2 * 2); }
 
 // Pick the number of key-range splits: enough workgroups to fill every CU
 // for the last wave without making the partial round trips dominate.
@@ -227,9 +225,15 @@ bca_status check_euler(float* z, const void* x, const float* w, int64_t n_tok, i
   return BCA_OK;
 }
 
+bool euler_mfma_ok(const float* w, int32_t k, int32_t n_ch, int32_t x_dtype) {
+  return w && x_dtype == BCA_BF16 && n_ch == 16 && k % 32 == 0;
+}
+
+// wt: transposed W halves already in the workspace (performer_unit prepares
+// them once per unit), or nullptr to prepare them here when there is room.
 bca_status enqueue_euler(float* z, const void* x, const float* w, int64_t n_tok, int32_t k,
                          int32_t n_ch, float dtau, int32_t x_dtype, void* workspace,
-                         size_t workspace_bytes, hipStream_t s) {
+                         size_t workspace_bytes, bool wt_ready, hipStream_t s) {
   if (n_tok == 0) return BCA_OK;
   EulerArgs a{};
   a.z = z;
@@ -242,32 +246,12 @@ bca_status enqueue_euler(float* z, const void* x, const float* w, int64_t n_tok,
   hipError_t e;
   if (!w) {
     e = launch_euler_plain(a, s);
-  } else if (x_dtype == BCA_BF16 && n_ch == 16 && k % 32 == 0) {
-    const int64_t ntb = (n_tok + kEulerTokens - 1) / kEulerTokens;
-    const int cus = cu_count();
-    int ksplit = (int)std::max<int64_t>((k + kEulerMaxChunk - 1) / kEulerMaxChunk,
-                                        (2 * cus + ntb - 1) / ntb);
-    ksplit = std::min(ksplit, std::min(kMaxEulerSplit, k / 32));
-    int kchunk = ((k + ksplit - 1) / ksplit + 31) / 32 * 32;
-    ksplit = (k + kchunk - 1) / kchunk;
-    const size_t cbytes = euler_counter_bytes(n_tok);
-    const size_t pbytes = (size_t)ksplit * n_tok * 16 * 4;
-    if (ksplit > 1 && (!workspace || workspace_bytes < cbytes + pbytes)) {
-      // no room for partials: one split if the chunk fits, else the generic path
-      if (k <= kEulerMaxChunk) { ksplit = 1; kchunk = k; }
-      else ksplit = 0;
-    }
-    if (ksplit >= 1) {
-      a.ksplit = ksplit;
-      a.kchunk = kchunk;
-      if (ksplit > 1) {
-        a.counters = static_cast<int32_t*>(workspace);
-        a.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + cbytes);
-      }
-      e = launch_euler_bf16_proj(a, s);
-    } else {
-      e = launch_euler_generic(a, false, s);
-    }
+  } else if (euler_mfma_ok(w, k, n_ch, x_dtype) && workspace && workspace_bytes >= euler_wt_bytes(k)) {
+    a.wt_hi = static_cast<const uint16_t*>(workspace);
+    a.wt_lo = a.wt_hi + (size_t)k * 16;
+    e = wt_ready ? hipSuccess
+                 : launch_w_prep(w, const_cast<uint16_t*>(a.wt_hi), const_cast<uint16_t*>(a.wt_lo), k, s);
+    if (e == hipSuccess) e = launch_euler_proj(a, s);
   } else {
     e = launch_euler_generic(a, x_dtype == BCA_F32, s);
   }
@@ -292,9 +276,7 @@ const char* bca_status_string(int32_t st) {
 size_t bca_workspace_bytes(const bca_kv_cache* c, int64_t n_q, int64_t n_kv, int32_t n_ch) {
   if (!c || n_q <= 0 || n_kv <= 0 || c->n_heads <= 0 || c->head_dim <= 0) return 0;
   (void)n_ch;
-  const size_t attn = attn_split_bytes(c, n_q, kMaxAttnSplit);
-  const size_t euler = (size_t)kMaxEulerSplit * n_q * 16 * 4;
-  return euler_counter_bytes(n_q) + std::max(attn, euler);
+  return euler_wt_bytes((int64_t)c->n_heads * c->head_dim) + attn_split_bytes(c, n_q, kMaxAttnSplit);
 }
 
 bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_new, int64_t n_new,
@@ -311,12 +293,11 @@ bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t
   bca_status st = check_attn(q, n_q, q_pos0, block_size, c, n_kv, out, q_dtype, out_dtype,
                              softmax_scale);
   if (st != BCA_OK) return st;
-  // the attention split region sits after the Euler counters so that a
-  // shared workspace keeps the counters' zeros
+  // the attention region follows the Euler region (W's transposed halves)
   char* ws = static_cast<char*>(workspace);
   size_t room = workspace_bytes;
   if (ws) {
-    const size_t skip = euler_counter_bytes(n_q);
+    const size_t skip = euler_wt_bytes((int64_t)c->n_heads * c->head_dim);
     if (room > skip) { ws += skip; room -= skip; } else { ws = nullptr; room = 0; }
   }
   return enqueue_attn(q, n_q, q_pos0, block_size, c, n_kv, out, out_dtype, softmax_scale, ws,
@@ -328,7 +309,8 @@ bca_status fm_euler_step(float* z, const void* x, const float* w, int64_t n_tok,
                          size_t workspace_bytes, hipStream_t s) {
   bca_status st = check_euler(z, x, w, n_tok, k, n_ch, dtau, x_dtype);
   if (st != BCA_OK) return st;
-  return enqueue_euler(z, x, w, n_tok, k, n_ch, dtau, x_dtype, workspace, workspace_bytes, s);
+  return enqueue_euler(z, x, w, n_tok, k, n_ch, dtau, x_dtype, workspace, workspace_bytes, false,
+                       s);
 }
 
 bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new, const void* q,
@@ -354,20 +336,24 @@ bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new,
   st = enqueue_append(c, k_new, v_new, n_q, s);
   if (st != BCA_OK) return st;
   char* ws = static_cast<char*>(workspace);
-  size_t room = workspace_bytes;
-  char* attn_ws = nullptr;
-  size_t attn_room = 0;
-  if (ws) {
-    const size_t skip = euler_counter_bytes(n_q);
-    if (room > skip) { attn_ws = ws + skip; attn_room = room - skip; }
+  size_t room = workspace ? workspace_bytes : 0;
+  const size_t wt_bytes = euler_wt_bytes(kdim);
+  const bool wt = euler_mfma_ok(w, kdim, n_ch, io) && room >= wt_bytes;
+  if (wt) {
+    // W's transposed halves, once per unit
+    uint16_t* hi = reinterpret_cast<uint16_t*>(ws);
+    if (launch_w_prep(w, hi, hi + (size_t)kdim * 16, kdim, s) != hipSuccess) return BCA_EHIP;
   }
+  char* attn_ws = room > wt_bytes ? ws + wt_bytes : nullptr;
+  const size_t attn_room = room > wt_bytes ? room - wt_bytes : 0;
   for (int32_t step = 0; step < n_steps; ++step) {
     if (attn_events && hipEventRecord(attn_events[2 * step], s) != hipSuccess) return BCA_EHIP;
     st = enqueue_attn(q, n_q, n_kv - n_q, (int32_t)n_q, c, n_kv, o_scratch, io, 0.0f, attn_ws,
                       attn_room, s);
     if (st != BCA_OK) return st;
     if (attn_events && hipEventRecord(attn_events[2 * step + 1], s) != hipSuccess) return BCA_EHIP;
-    st = enqueue_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io, ws, room, s);
+    st = enqueue_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io, wt ? ws : nullptr,
+                       wt ? wt_bytes : 0, wt, s);
     if (st != BCA_OK) return st;
   }
   return BCA_OK;

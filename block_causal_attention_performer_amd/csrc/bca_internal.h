@@ -15,7 +15,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeyTile = 64;        // keys per attention tile (a tile never straddles a >=64 page)
-constexpr int kEulerTokens = 64;    // tokens per workgroup in the fused Euler kernel
 constexpr int kAttnFlagWaves = 8;   // overflow flags per (query tile, split) of the fast attention kernel
 
 // ---------------------------------------------------------------- launchers
@@ -76,16 +75,16 @@ struct EulerArgs {
   float* z;
   const void* x;
   const float* w;
-  float* ws_part;    // [ksplit][n_tok][16] fp32
-  int32_t* counters; // [ceil(n_tok/64)], zero between calls
+  const uint16_t* wt_hi;   // W transposed to [16][k], bf16 high half
+  const uint16_t* wt_lo;   // bf16 low half (W - hi)
   int64_t n_tok;
   int32_t k;
   int32_t n_ch;
-  int32_t ksplit;
-  int32_t kchunk;    // k per split (multiple of 32)
   float dtau;
 };
-hipError_t launch_euler_bf16_proj(const EulerArgs& a, hipStream_t s);
+// W [k][16] fp32 -> wt_hi/wt_lo [16][k] bf16 (k * 64 bytes in total).
+hipError_t launch_w_prep(const float* w, uint16_t* wt_hi, uint16_t* wt_lo, int k, hipStream_t s);
+hipError_t launch_euler_proj(const EulerArgs& a, hipStream_t s);
 hipError_t launch_euler_generic(const EulerArgs& a, bool x_f32, hipStream_t s);
 hipError_t launch_euler_plain(const EulerArgs& a, hipStream_t s);
 

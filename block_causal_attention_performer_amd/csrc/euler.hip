@@ -8,19 +8,20 @@
 //
 // bf16 x, n_ch = 16: the product runs on v_mfma_f32_16x16x32_bf16 with W
 // split into bf16 high and low halves (W = hi + lo to ~2^-16 relative), two
-// MFMAs per k-step, fp32 accumulation.  The kernel is bound by reading x
-// from HBM; W (fp32) is re-read from L2 and staged transposed in LDS.  k is
-// split across workgroups; the last workgroup of a token block (atomic
-// counter) sums the partials in split order and applies the update, then
-// resets the counter, so results do not depend on arrival order.
+// MFMAs per k-step, fp32 accumulation.  W is first rewritten transposed,
+// as hi/lo bf16 rows per channel (w_prep_kernel, 64 bytes per row of W, into
+// the caller's workspace), so every MFMA operand is one 16-byte load.  The
+// main kernel is bound by reading x from HBM once: one workgroup per 16
+// tokens, its four waves split k and add their 16x16 partials through LDS
+// in a fixed order before the update.
 #include "bca_internal.h"
 
 namespace bca {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kMaxSteps = 20;       // k-steps of 32 per split (kchunk <= 640)
-constexpr int kWPitch = kMaxSteps * 32 + 8;   // LDS row pitch (bf16), +16 bytes
+constexpr int kTok = 16;       // tokens per workgroup
+constexpr int kBatch = 8;      // k-steps loaded ahead per wave
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   const uint32_t b = __float_as_uint(f);
@@ -28,85 +29,58 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(kThreads) void euler_bf16_proj_kernel(EulerArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t whi[16 * kWPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t wlo[16 * kWPitch];
-  __shared__ int s_last;
+// W [k][16] fp32 -> wt_hi / wt_lo [16][k] bf16 with W = hi + lo (+ O(2^-16)).
+__global__ __launch_bounds__(kThreads) void w_prep_kernel(const float* w, uint16_t* wt_hi,
+                                                          uint16_t* wt_lo, int k) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= k * 16) return;
+  const int kk = i >> 4, c = i & 15;
+  const float f = w[i];
+  const uint16_t hi = bf16_rne(f);
+  wt_hi[(int64_t)c * k + kk] = hi;
+  wt_lo[(int64_t)c * k + kk] = bf16_rne(f - __uint_as_float((uint32_t)hi << 16));
+}
+
+__global__ __launch_bounds__(kThreads) void euler_proj_kernel(EulerArgs a) {
+  __shared__ float part[4][kTok * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tb = blockIdx.x, sp = blockIdx.y;
-  const int kbeg = sp * a.kchunk;
-  const int kend = min(a.k, kbeg + a.kchunk);
-  const int nsteps = (kend - kbeg) / 32;
-  const int64_t row = (int64_t)tb * kEulerTokens + wave * 16 + (lane & 15);
+  const int64_t row = (int64_t)blockIdx.x * kTok + (lane & 15);
   const bool rv = row < a.n_tok;
-  const uint16_t* x = static_cast<const uint16_t*>(a.x);
-
-  // issue every x load of this split first (A operand: row, 8 k per lane)
-  u32x4 xr[kMaxSteps];
-  const uint16_t* xp = x + row * a.k + kbeg + 8 * (lane >> 4);
-#pragma unroll
-  for (int j = 0; j < kMaxSteps; ++j)
-    xr[j] = (rv && j < nsteps) ? *reinterpret_cast<const u32x4*>(xp + 32 * j) : u32x4{0, 0, 0, 0};
-
-  // W[kbeg:kend, 0:16] -> LDS as W^T hi/lo bf16, rows = channel
-  for (int u = tid; u < 16 * nsteps * 4; u += kThreads) {
-    const int c = u & 15, oct = u >> 4;
-    const float* wp = a.w + (int64_t)(kbeg + 8 * oct) * 16 + c;
-    uint16_t hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float f = wp[16 * e];
-      hi[e] = bf16_rne(f);
-      lo[e] = bf16_rne(f - __uint_as_float((uint32_t)hi[e] << 16));
-    }
-    *reinterpret_cast<u32x4*>(&whi[c * kWPitch + 8 * oct]) = *reinterpret_cast<const u32x4*>(hi);
-    *reinterpret_cast<u32x4*>(&wlo[c * kWPitch + 8 * oct]) = *reinterpret_cast<const u32x4*>(lo);
-  }
-  __syncthreads();
+  const int nsteps = a.k / 32;
+  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+  const int oct = 8 * (lane >> 4);
+  const uint16_t* xp = static_cast<const uint16_t*>(a.x) + row * a.k + oct;
+  const uint16_t* hp = a.wt_hi + (int64_t)(lane & 15) * a.k + oct;
+  const uint16_t* lp = a.wt_lo + (int64_t)(lane & 15) * a.k + oct;
 
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int wrow = (lane & 15) * kWPitch + 8 * (lane >> 4);
+  for (int sb = s0; sb < s1; sb += kBatch) {
+    u32x4 xr[kBatch], hr[kBatch], lr[kBatch];
 #pragma unroll
-  for (int j = 0; j < kMaxSteps; ++j) {
-    if (j < nsteps) {
+    for (int j = 0; j < kBatch; ++j) {
+      const int st = sb + j;
+      const bool ok = st < s1;
+      xr[j] = (ok && rv) ? *reinterpret_cast<const u32x4*>(xp + 32 * st) : u32x4{0, 0, 0, 0};
+      hr[j] = ok ? *reinterpret_cast<const u32x4*>(hp + 32 * st) : u32x4{0, 0, 0, 0};
+      lr[j] = ok ? *reinterpret_cast<const u32x4*>(lp + 32 * st) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
       const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[j]);
-      const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&whi[wrow + 32 * j]));
-      const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&wlo[wrow + 32 * j]));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, hr[j]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, lr[j]), acc, 0, 0, 0);
     }
   }
-
-  // acc[e] = v[token 4*(lane>>4)+e of this wave's 16][channel lane&15]
-  const int c = lane & 15;
-  const int64_t tok0 = (int64_t)tb * kEulerTokens + wave * 16 + 4 * (lane >> 4);
-  if (a.ksplit == 1) {
+  // acc[e] = partial v[token 4*(lane>>4)+e][channel lane&15]
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (tok0 + e < a.n_tok) {
-        float* zp = a.z + (tok0 + e) * 16 + c;
-        *zp = __builtin_fmaf(-a.dtau, acc[e], *zp);
-      }
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (tok0 + e < a.n_tok) a.ws_part[((int64_t)sp * a.n_tok + tok0 + e) * 16 + c] = acc[e];
-  __threadfence();
+  for (int e = 0; e < 4; ++e) part[wave][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[tb], 1) == a.ksplit - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int i = tid; i < kEulerTokens * 16; i += kThreads) {
-    const int64_t tok = (int64_t)tb * kEulerTokens + i / 16;
-    if (tok >= a.n_tok) continue;
-    float v = 0.0f;
-    for (int s = 0; s < a.ksplit; ++s) v += a.ws_part[((int64_t)s * a.n_tok + tok) * 16 + (i & 15)];
-    float* zp = a.z + tok * 16 + (i & 15);
+  const int64_t tok = (int64_t)blockIdx.x * kTok + (tid >> 4);
+  if (tok < a.n_tok) {
+    const float v = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+    float* zp = a.z + tok * 16 + (tid & 15);
     *zp = __builtin_fmaf(-a.dtau, v, *zp);
   }
-  if (tid == 0) a.counters[tb] = 0;
 }
 
 // Any x dtype / n_ch <= 64 / k: one workgroup per token, fp32 FMA, fixed
@@ -151,11 +125,15 @@ __global__ __launch_bounds__(kThreads) void euler_plain_kernel(EulerArgs a) {
   a.z[i] = __builtin_fmaf(-a.dtau, static_cast<const float*>(a.x)[i], a.z[i]);
 }
 
-hipError_t launch_euler_bf16_proj(const EulerArgs& a, hipStream_t s) {
-  if (a.n_ch != 16 || a.k % 32 != 0 || a.kchunk % 32 != 0 || a.kchunk > kMaxSteps * 32)
-    return hipErrorInvalidValue;
-  dim3 grid((unsigned)((a.n_tok + kEulerTokens - 1) / kEulerTokens), (unsigned)a.ksplit);
-  euler_bf16_proj_kernel<<<grid, kThreads, 0, s>>>(a);
+hipError_t launch_w_prep(const float* w, uint16_t* wt_hi, uint16_t* wt_lo, int k, hipStream_t s) {
+  const int n = k * 16;
+  w_prep_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(w, wt_hi, wt_lo, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_euler_proj(const EulerArgs& a, hipStream_t s) {
+  if (a.n_ch != 16 || a.k % 32 != 0 || !a.wt_hi || !a.wt_lo) return hipErrorInvalidValue;
+  euler_proj_kernel<<<(unsigned)((a.n_tok + kTok - 1) / kTok), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

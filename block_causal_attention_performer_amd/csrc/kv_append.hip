@@ -4,84 +4,95 @@
 // cache (deep read "全双工语音模型精读⑫：Wan-Streamer", section 4, step 3).
 // K pages are token-major [page][h][slot][d]; V pages are d-major
 // [page][h][d][slot] so that the attention kernel reads 16-byte runs along
-// the key axis.  Both copies are pure data movement (HBM bound): every
-// workgroup moves one 64-token logical chunk of one head.
+// the key axis.  The bf16/fp32 copy is pure data movement (HBM bound): each
+// lane moves a 16-byte-square block of K and of V, transposing V in
+// registers, so every load and store is a 16-byte vector.
 #include "bca_internal.h"
 
 namespace bca {
 namespace {
 
-constexpr int kChunk = 64;
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int64_t page_slot_offset(const int32_t* pt, int64_t t,
-                                                    int ps_log2, int h, int H,
-                                                    int row_elems) {
-  // element offset of (token t, head h) row start in a [page][h][ps][row] array
-  const int64_t page = pt[t >> ps_log2];
-  const int64_t slot = t & ((1 << ps_log2) - 1);
-  return ((page * H + h) << ps_log2 | slot) * (int64_t)row_elems;
+// Transpose an E x E block held as E rows of 16 bytes (row = token,
+// column = head dim) into E rows of head dims, each holding E tokens.
+template <typename T>
+__device__ __forceinline__ void transpose_block(const u32x4 (&in)[16 / sizeof(T)],
+                                                u32x4 (&out)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    // out[d].word[w] = (token 2w, token 2w+1) of column d
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        out[d][w] = __builtin_amdgcn_perm(in[2 * w + 1][d >> 1], in[2 * w][d >> 1],
+                                          (d & 1) ? 0x07060302u : 0x05040100u);
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) out[d][w] = in[w][d];
+  }
 }
 
+// One wave per (TPW consecutive tokens, head), over the tokens [g0, g1) of
+// the slice whose E-aligned groups it covers fully.  Lane (to, j) moves the
+// E tokens t0 = g0 + to*E .. +E-1, head dims j*E .. +E-1: E 16-byte loads of
+// K and of V; K rows are stored as they are, the V block is transposed in
+// registers and stored as E runs of E tokens of the V^T rows.  The E tokens
+// lie in one page (pages hold >= 16 tokens, groups are E-aligned).
 // T: element type (uint16_t for bf16, float for f32); D: head dim.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void append_copy_kernel(AppendArgs a) {
+__global__ __launch_bounds__(64) void append_copy_kernel(AppendArgs a, int64_t g0, int64_t g1) {
   constexpr int E = 16 / sizeof(T);          // elements per 16-byte vector
-  constexpr int RV = D / E;                  // 16-byte vectors per K row
-  constexpr int LD = D + 4 / sizeof(T);      // LDS row pitch (+4 bytes: spreads banks)
-  __shared__ T tile[kChunk * LD];
-
+  constexpr int JO = D / E;                  // 16-byte chunks per token row
+  constexpr int TO = 64 / JO;                // token groups per wave
+  constexpr int TPW = TO * E;                // tokens per workgroup
+  const int lane = threadIdx.x;
+  const int j = lane % JO, to = lane / JO;
   const int h = blockIdx.y;
   const int H = a.n_heads;
-  const int64_t base = (a.n0 & ~(int64_t)(kChunk - 1)) + (int64_t)blockIdx.x * kChunk;
-  const int64_t lo = a.n0, hi = a.n0 + a.n_new;
-  const T* kin = static_cast<const T*>(a.k_new);
-  const T* vin = static_cast<const T*>(a.v_new);
-  T* kp = static_cast<T*>(a.k_pages);
-  T* vp = static_cast<T*>(a.v_pages);
+  const int64_t t0 = g0 + (int64_t)blockIdx.x * TPW + to * E;
+  if (t0 >= g1) return;
+  const int64_t page = a.page_table[t0 >> a.ps_log2];
+  const int64_t slot0 = t0 & ((1 << a.ps_log2) - 1);
+  const T* kin = static_cast<const T*>(a.k_new) + ((t0 - a.n0) * H + h) * D + j * E;
+  const T* vin = static_cast<const T*>(a.v_new) + ((t0 - a.n0) * H + h) * D + j * E;
+  const int64_t in_stride = (int64_t)H * D;
 
-  // K rows: straight copy, one 16-byte vector per thread per pass.
-  for (int i = threadIdx.x; i < kChunk * RV; i += kThreads) {
-    const int r = i / RV, c = i % RV;
-    const int64_t t = base + r;
-    if (t < lo || t >= hi) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(kin + ((t - lo) * H + h) * D + c * E);
-    *reinterpret_cast<u32x4*>(kp + page_slot_offset(a.page_table, t, a.ps_log2, h, H, D) + c * E) = v;
-  }
-  // V rows into LDS (rows outside the slice are never written out).
-  for (int i = threadIdx.x; i < kChunk * RV; i += kThreads) {
-    const int r = i / RV, c = i % RV;
-    const int64_t t = base + r;
-    if (t < lo || t >= hi) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(vin + ((t - lo) * H + h) * D + c * E);
-    const T* pv = reinterpret_cast<const T*>(&v);
+  u32x4 kr[E], vr[E], vt[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) tile[r * LD + c * E + e] = pv[e];
+  for (int e = 0; e < E; ++e) {
+    kr[e] = *reinterpret_cast<const u32x4*>(kin + e * in_stride);
+    vr[e] = *reinterpret_cast<const u32x4*>(vin + e * in_stride);
   }
-  __syncthreads();
-  // V^T: for each d, E consecutive tokens form one 16-byte run of a page row.
-  constexpr int RUNS = kChunk / E;           // runs per d-row of the chunk
-  const int ps = 1 << a.ps_log2;
-  for (int i = threadIdx.x; i < D * RUNS; i += kThreads) {
-    const int d = i / RUNS, run = i % RUNS;
-    const int64_t t0 = base + run * E;
-    if (t0 + E <= lo || t0 >= hi) continue;
-    // E tokens never straddle a page (page_size >= 16 >= E)
-    const int64_t page = a.page_table[t0 >> a.ps_log2];
-    const int64_t slot = t0 & (ps - 1);
-    T* dst = vp + (((page * H + h) * D + d) << a.ps_log2) + slot;
-    if (t0 >= lo && t0 + E <= hi) {
-      T buf[E];
+  T* krow = static_cast<T*>(a.k_pages) + (((page * H + h) << a.ps_log2) + slot0) * D + j * E;
 #pragma unroll
-      for (int e = 0; e < E; ++e) buf[e] = tile[(run * E + e) * LD + d];
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(buf);
-    } else {
-      for (int e = 0; e < E; ++e) {
-        const int64_t t = t0 + e;
-        if (t >= lo && t < hi) dst[e] = tile[(run * E + e) * LD + d];
-      }
-    }
-  }
+  for (int e = 0; e < E; ++e) *reinterpret_cast<u32x4*>(krow + e * D) = kr[e];
+  transpose_block<T>(vr, vt);
+  T* vcol = static_cast<T*>(a.v_pages) + ((((page * H + h) * D + j * E) << a.ps_log2) + slot0);
+#pragma unroll
+  for (int e = 0; e < E; ++e) *reinterpret_cast<u32x4*>(vcol + (e << a.ps_log2)) = vt[e];
+}
+
+// Tokens of the slice outside [g0, g1) (fewer than E at each end): one
+// workgroup per (token, head), one element per thread.
+template <typename T>
+__global__ void append_edge_kernel(AppendArgs a, int64_t g0, int64_t g1) {
+  const int64_t lo = a.n0, hi = a.n0 + a.n_new;
+  const int64_t n_head_edge = (g0 < hi ? g0 : hi) - lo;
+  const int64_t t = blockIdx.x < n_head_edge ? lo + blockIdx.x
+                                             : (g1 > g0 ? g1 : g0) + (blockIdx.x - n_head_edge);
+  const int d = threadIdx.x;
+  if (t >= hi || d >= a.head_dim) return;
+  const int h = blockIdx.y, H = a.n_heads, D = a.head_dim;
+  const int64_t page = a.page_table[t >> a.ps_log2];
+  const int64_t slot = t & ((1 << a.ps_log2) - 1);
+  const int64_t src = ((t - lo) * H + h) * D + d;
+  static_cast<T*>(a.k_pages)[(((page * H + h) << a.ps_log2) + slot) * D + d] =
+      static_cast<const T*>(a.k_new)[src];
+  static_cast<T*>(a.v_pages)[(((page * H + h) * D + d) << a.ps_log2) + slot] =
+      static_cast<const T*>(a.v_new)[src];
 }
 
 // ------------------------------------------------------------------ fp8
@@ -198,27 +209,40 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(AppendArgs a) {
   }
 }
 
+template <typename T, int D>
+hipError_t launch_copy_t(const AppendArgs& a, hipStream_t s) {
+  constexpr int E = 16 / (int)sizeof(T);
+  constexpr int TPW = 64 / (D / E) * E;
+  const int64_t lo = a.n0, hi = a.n0 + a.n_new;
+  const int64_t g0 = (lo + E - 1) / E * E, g1 = hi / E * E;
+  if (g1 > g0) {
+    dim3 grid((unsigned)((g1 - g0 + TPW - 1) / TPW), (unsigned)a.n_heads);
+    append_copy_kernel<T, D><<<grid, 64, 0, s>>>(a, g0, g1);
+  }
+  const int64_t n_edge = g1 > g0 ? (g0 - lo) + (hi - g1) : a.n_new;
+  if (n_edge > 0) {
+    dim3 grid((unsigned)n_edge, (unsigned)a.n_heads);
+    append_edge_kernel<T><<<grid, D, 0, s>>>(a, g0, g1);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_append_copy(const AppendArgs& a, int elem_bytes, hipStream_t s) {
-  const int64_t first = a.n0 & ~(int64_t)(kChunk - 1);
-  const int64_t nchunks = (a.n0 + a.n_new - first + kChunk - 1) / kChunk;
-  dim3 grid((unsigned)nchunks, (unsigned)a.n_heads);
   if (elem_bytes == 2) {
     switch (a.head_dim) {
-      case 64: append_copy_kernel<uint16_t, 64><<<grid, kThreads, 0, s>>>(a); break;
-      case 128: append_copy_kernel<uint16_t, 128><<<grid, kThreads, 0, s>>>(a); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (a.head_dim) {
-      case 32: append_copy_kernel<float, 32><<<grid, kThreads, 0, s>>>(a); break;
-      case 64: append_copy_kernel<float, 64><<<grid, kThreads, 0, s>>>(a); break;
-      case 128: append_copy_kernel<float, 128><<<grid, kThreads, 0, s>>>(a); break;
+      case 64: return launch_copy_t<uint16_t, 64>(a, s);
+      case 128: return launch_copy_t<uint16_t, 128>(a, s);
       default: return hipErrorInvalidValue;
     }
   }
-  return hipGetLastError();
+  switch (a.head_dim) {
+    case 32: return launch_copy_t<float, 32>(a, s);
+    case 64: return launch_copy_t<float, 64>(a, s);
+    case 128: return launch_copy_t<float, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t s) {

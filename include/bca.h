@@ -133,10 +133,16 @@ BCA_API bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_n
  *        Streaming call: q_pos0 = n_kv - n_q, block_size = n_q (all visible).
  *        Full sequence:  q_pos0 = 0, n_q = n_kv.  block_size = 1 is causal.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
- *   workspace: optional device scratch (may be NULL) of workspace_bytes;
- *        with room the key range is split across workgroups and merged by a
- *        fixed-order log-sum-exp combine (results do not depend on timing).
- *        bca_workspace_bytes() gives the size that enables every split.
+ *   workspace: optional device scratch (may be NULL) of workspace_bytes.
+ *        Without it a single kernel with an exact running-maximum softmax
+ *        runs.  With it (layout: 64*n_heads*head_dim bytes reserved for
+ *        fm_euler_step, then this call's region) a faster kernel runs that
+ *        keeps the first key tile's row maximum as its softmax reference and
+ *        flags any query tile whose later logits exceed it by more than
+ *        2^40; flagged tiles are recomputed exactly.  The key range may also
+ *        be split across workgroups and merged by a fixed-order log-sum-exp
+ *        combine.  Results never depend on timing.  bca_workspace_bytes()
+ *        gives the size that enables every path.
  */
 BCA_API bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0,
                              int32_t block_size, const bca_kv_cache* c,
@@ -153,10 +159,11 @@ BCA_API bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0,
  *            or BCA_F32), w [k][n_ch] fp32.
  * w == NULL: v = x, x [n_tok][n_ch] fp32 (k ignored).
  * z [n_tok][n_ch] fp32, updated in place.  n_ch <= 64.
- * workspace: the bf16 path splits k across workgroups when workspace has
- * room (bca_workspace_bytes); the split partials are summed in fixed order.
- * The workspace must be zero-filled once before its first use (its counters
- * return to zero at the end of every call).
+ * workspace (may be NULL): with bf16 x, n_ch = 16, k % 32 == 0 and at least
+ * 64*k bytes, W is first rewritten into its first 64*k bytes (transposed
+ * bf16 high/low halves, W = hi + lo to ~2^-16) and the product runs on the
+ * matrix cores; otherwise a slower fp32 vector path runs.  Results do not
+ * depend on timing (fixed summation order).
  */
 BCA_API bca_status fm_euler_step(float* z, const void* x, const float* w,
                          int64_t n_tok, int32_t k, int32_t n_ch, float dtau,
@@ -175,8 +182,8 @@ BCA_API bca_status fm_euler_step(float* z, const void* x, const float* w,
  *   w:  [n_heads*head_dim][n_ch] fp32;  z: [n_q][n_ch] fp32, noise in,
  *       clean latents out
  *   o_scratch: [n_q][n_heads][head_dim] (f32 for an f32 cache, else bf16)
- *   workspace: as for block_causal_attn / fm_euler_step (zero-filled before
- *       first use; may be NULL)
+ *   workspace: as for block_causal_attn / fm_euler_step (may be NULL);
+ *       bca_workspace_bytes() gives the size for the fastest path
  *   attn_events: NULL, or 2*n_steps events; event 2s is recorded on s just
  *       before attention step s and event 2s+1 just after it (timing hook)
  * All arguments of all four phases are validated before the first launch.
