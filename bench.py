@@ -177,19 +177,21 @@ def main():
     attn_tflops = flops_call / (attn_avg * 1e-3) / 1e12
     value = S * flops_call / (ms_unit * 1e-3) / 1e12
 
-    # ---- append and Euler alone (events around each call; caches flushed
-    # between reps by writing a 1 GiB buffer)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # ---- append and Euler alone (events around each call).  Between reps
+    # the caches are flushed by READING a 1 GiB buffer: a write flush would
+    # leave dirty lines in the 256 MB last-level cache whose write-back then
+    # lands inside the timed kernel.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     e0, e1 = hip.event(), hip.event()
     app_ms, eul_ms = [], []
     for _ in range(args.kernel_reps):
-        flush.fill_(1)
+        flush.sum()
         cache.c.n_tokens = w.n_hist
         hip.record(e0, stream)
         bca.kv_append(cache, inp["k_new"], inp["v_new"])
         hip.record(e1, stream)
         app_ms.append(hip.elapsed_ms(e0, e1))
-        flush.fill_(2)
+        flush.sum()
         hip.record(e0, stream)
         bca.fm_euler_step(z, osc, inp["w"], 1.0 / S, workspace=ws)
         hip.record(e1, stream)

@@ -49,6 +49,10 @@ constexpr int NW = 8;             // waves per workgroup (two groups of four)
 constexpr int NT = NW * 64;
 constexpr int GT = NT / 2;        // threads per group
 constexpr int BM = NW * QW;       // query rows per workgroup
+#ifndef BCA_ATTN_NIF
+#define BCA_ATTN_NIF 6
+#endif
+constexpr int NIF = BCA_ATTN_NIF; // LDS reads kept in flight ahead of the MFMAs
 constexpr float kSlowSum = 1099511627776.0f;   // 2^40
 static_assert(NW == kAttnFlagWaves, "one overflow flag per wave");
 
@@ -77,6 +81,15 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Page-table entry through the scalar cache: the table is read-only for the
+// whole launch and the index is uniform, so the physical page (and every
+// tile base address derived from it) lives in scalar registers.
+__device__ __forceinline__ int64_t page_of(const int32_t* pt, int64_t lp) {
+  return ((const __attribute__((address_space(4))) int32_t*)(const void*)pt)[lp];
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // fp8 E4M3FN -> bf16 bits for 4 codes packed in a u32.  Exact (3 mantissa
 // bits fit in bf16's 7; the E4M3 exponent range fits bf16's).
@@ -165,14 +178,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
   bool overflow = false;     // a tile exceeded the first tile's maximum by > 2^40
 
-  // per-lane LDS read offsets (elements within one slot); +32 rows per MFMA
-  // row block is a constant offset.
+  // per-lane LDS read addresses (bytes): chunk j of the lane's row sits at
+  // row_base + ((16 j) ^ x) with x = 16 (swizzle(row) ^ half) -- the lane's
+  // half is the low bit of j.  A slot offset (a multiple of the 16 KB slot
+  // size, above every in-slot bit) is folded into x by XOR once per tile;
+  // +32 rows per MFMA row block is an immediate offset.
   const int kr = sigma32(col);
-  int koff[KK], voff[4];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) koff[kk] = kr * D + (((2 * kk + half) ^ swz<RK>(kr)) * 8);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) voff[c] = kr * BN + (((2 * c + half) ^ swz<8>(kr)) * 8);
+  const uint32_t krow = (uint32_t)(kr * D * 2), kx = (uint32_t)((swz<RK>(kr) ^ half) * 16);
+  const uint32_t vrow = (uint32_t)(kr * BN * 2), vx = (uint32_t)((swz<8>(kr) ^ half) * 16);
 
   const int ps_log2 = a.ps_log2;
   const int psm = (1 << ps_log2) - 1;
@@ -180,84 +193,64 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
   const uint8_t* vpages = static_cast<const uint8_t*>(a.v_pages);
 
   // ------------------------------------------------------------ tile staging
-  // HBM -> registers -> LDS by one group (256 threads); fp8 is widened to
-  // bf16 and keys past n_kv are zeroed on the way.
+  // HBM -> registers -> LDS by one group (256 threads): group A stages K
+  // tiles, group B V^T tiles.  Every tile is loaded by one sequence of
+  // unconditional 16-byte loads (keys past n_kv read whatever their page
+  // holds, or a clamped key on small pages) so the staging registers have a
+  // single definition in the loop; the LDS store widens fp8 to bf16.
   u32x4 rg[TG];
   float sc_pend = 1.0f;      // fp8 scale of the staged tile
-  auto load_k = [&](int t) {
+  int64_t k0_pend = 0;       // first key of the staged tile
+  // per-lane byte offset of load 0 inside a tile; load i adds a uniform step
+  static_assert(GT % KPR == 0 && GT % VPR == 0, "loads step by whole rows");
+  const uint32_t goff = group_b ? (uint32_t)(((gt / VPR) << ps_log2) * EB + (gt % VPR) * 16)
+                                : (uint32_t)((gt / KPR) * D * EB + (gt % KPR) * 16);
+  const int64_t gstep = group_b ? ((int64_t)(GT / VPR) << ps_log2) * EB : (int64_t)(GT / KPR) * D * EB;
+  const uint8_t* gpages = group_b ? vpages : kpages;
+  const float* gscales = group_b ? a.v_scales : a.k_scales;
+  auto load_tile = [&](int t) {
     const int64_t k0 = (int64_t)t * BN;
-    if (!SMALLPAGE && k0 + BN <= a.n_kv) {
-      const int64_t page = a.page_table[k0 >> ps_log2];
-      const uint8_t* kb = kpages + ((((page * H + h) << ps_log2) | (k0 & psm)) * D) * EB;
+    k0_pend = k0;
+    const int64_t page = page_of(a.page_table, k0 >> ps_log2);
+    if constexpr (FP8) sc_pend = gscales[page * H + h];
+    if constexpr (!SMALLPAGE) {
+      // a whole tile lies in one page: uniform base, per-lane offsets
+      const int64_t ph = page * H + h;
+      const uint8_t* base = gpages + (group_b ? (((ph * D) << ps_log2) + (k0 & psm)) * EB
+                                              : (((ph << ps_log2) | (k0 & psm)) * D) * EB);
+#pragma unroll
+      for (int i = 0; i < TG; ++i) rg[i] = ld16(base + i * gstep + goff);
+    } else {
+      // pages shorter than a tile: page per key (clamped to the last key)
 #pragma unroll
       for (int i = 0; i < TG; ++i) {
         const int c = gt + i * GT;
-        rg[i] = ld16(kb + (c / KPR) * D * EB + (c % KPR) * 16);
-      }
-      if constexpr (FP8) sc_pend = a.k_scales[page * H + h];
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < TG; ++i) {
-      const int c = gt + i * GT;
-      const int64_t key = k0 + c / KPR;
-      rg[i] = u32x4{0, 0, 0, 0};
-      if (key < a.n_kv) {
-        const int64_t page = a.page_table[key >> ps_log2];
-        rg[i] = ld16(kpages + ((((page * H + h) << ps_log2) | (key & psm)) * D) * EB + (c % KPR) * 16);
+        const int64_t key0 = group_b ? k0 + (c % VPR) * (16 / EB) : k0 + c / KPR;
+        const int64_t key = key0 < a.n_kv ? key0 : a.n_kv - 1;
+        const int64_t pg = a.page_table[key >> ps_log2];
+        const int64_t off = group_b
+            ? ((((pg * H + h) * D + c / VPR) << ps_log2) + (key & psm)) * EB
+            : ((((pg * H + h) << ps_log2) | (key & psm)) * D) * EB + (c % KPR) * 16;
+        rg[i] = ld16(gpages + off);
       }
     }
-    if constexpr (FP8) sc_pend = a.k_scales[a.page_table[k0 >> ps_log2] * H + h];
   };
-  auto load_v = [&](int t) {
-    const int64_t k0 = (int64_t)t * BN;
-    constexpr int per = 16 / EB;             // keys per 16 bytes
-    if (!SMALLPAGE && k0 + BN <= a.n_kv) {
-      const int64_t page = a.page_table[k0 >> ps_log2];
-      const uint8_t* vb = vpages + ((((page * H + h) * D) << ps_log2) + (k0 & psm)) * EB;
-#pragma unroll
-      for (int i = 0; i < TG; ++i) {
-        const int c = gt + i * GT;
-        rg[i] = ld16(vb + (((int64_t)(c / VPR)) << ps_log2) * EB + (c % VPR) * 16);
-      }
-      if constexpr (FP8) sc_pend = a.v_scales[page * H + h];
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < TG; ++i) {
-      const int c = gt + i * GT;
-      const int d = c / VPR, cc = c % VPR;
-      const int64_t key = k0 + cc * per;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (key < a.n_kv) {
-        const int64_t page = a.page_table[key >> ps_log2];
-        v = ld16(vpages + ((((page * H + h) * D + d) << ps_log2) + (key & psm)) * EB);
-        if (key + per > a.n_kv) {
-          // zero the values of keys past n_kv (they could hold anything)
-          constexpr int kpw = 4 / EB;        // keys per 32-bit word
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-#pragma unroll
-            for (int e = 0; e < kpw; ++e)
-              if (key + w * kpw + e >= a.n_kv) v[w] &= ~(((1u << (8 * EB)) - 1) << (8 * EB * e));
-        }
-      }
-      rg[i] = v;
-    }
-    if constexpr (FP8) sc_pend = a.v_scales[a.page_table[k0 >> ps_log2] * H + h];
-  };
+  // K rows past n_kv are stored as loaded: their scores are replaced by
+  // -inf in the softmax, whatever the row holds.  V values past n_kv are
+  // zeroed (a zero weight times a non-finite value would not be zero).
   auto store_k = [&](uint16_t* kl) {
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
       const int c = gt + i * GT;
       const int row = c / KPR, cc = c % KPR;
+      const u32x4 v = rg[i];
       if constexpr (!FP8) {
-        *reinterpret_cast<u32x4*>(kl + (row * RK + (cc ^ swz<RK>(row))) * 8) = rg[i];
+        *reinterpret_cast<u32x4*>(kl + (row * RK + (cc ^ swz<RK>(row))) * 8) = v;
       } else {
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-          const uint2 lo = fp8x4_to_bf16x4(rg[i][2 * part]);
-          const uint2 hi = fp8x4_to_bf16x4(rg[i][2 * part + 1]);
+          const uint2 lo = fp8x4_to_bf16x4(v[2 * part]);
+          const uint2 hi = fp8x4_to_bf16x4(v[2 * part + 1]);
           const int ch = 2 * cc + part;
           *reinterpret_cast<u32x4*>(kl + (row * RK + (ch ^ swz<RK>(row))) * 8) = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
@@ -265,17 +258,29 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
     }
   };
   auto store_v = [&](uint16_t* vl) {
+    const bool tail = k0_pend + BN > a.n_kv;
+    constexpr int per = 16 / EB;             // keys per 16 bytes
+    constexpr int kpw = 4 / EB;              // keys per 32-bit word
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
       const int c = gt + i * GT;
       const int d = c / VPR, cc = c % VPR;
+      u32x4 v = rg[i];
+      if (tail) {
+        const int64_t key = k0_pend + cc * per;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int e = 0; e < kpw; ++e)
+            if (key + w * kpw + e >= a.n_kv) v[w] &= ~(((1u << (8 * EB)) - 1) << (8 * EB * e));
+      }
       if constexpr (!FP8) {
-        *reinterpret_cast<u32x4*>(vl + (d * 8 + (cc ^ swz<8>(d))) * 8) = rg[i];
+        *reinterpret_cast<u32x4*>(vl + (d * 8 + (cc ^ swz<8>(d))) * 8) = v;
       } else {
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
-          const uint2 lo = fp8x4_to_bf16x4(rg[i][2 * part]);
-          const uint2 hi = fp8x4_to_bf16x4(rg[i][2 * part + 1]);
+          const uint2 lo = fp8x4_to_bf16x4(v[2 * part]);
+          const uint2 hi = fp8x4_to_bf16x4(v[2 * part + 1]);
           const int ch = 2 * cc + part;
           *reinterpret_cast<u32x4*>(vl + (d * 8 + (ch ^ swz<8>(d))) * 8) = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
@@ -291,66 +296,71 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
     const int t0 = t_begin;
     // prologue (synchronous): K(t0) by group A; V(t0), V(t0+1) by group B
     if (!group_b) {
-      load_k(t0); store_k(lk);
+      load_tile(t0); store_k(lk);
       if (gt == 0) kscale[0] = sc_pend;
     } else {
-      load_v(t0); store_v(lv);
+      load_tile(t0); store_v(lv);
+      // slot 2 stands for V(t0-1): zeros, so the first tile's PV step
+      // (with P(t0-1) = 0) adds exact zeros whatever LDS held before
       if (gt == 0) vscale[0] = sc_pend;
-      if (t0 + 1 < t_end) {
-        load_v(t0 + 1); store_v(lv + D * BN);
-        if (gt == 0) vscale[1] = sc_pend;
-      }
+#pragma unroll
+      for (int i = 0; i < TG; ++i) rg[i] = u32x4{0, 0, 0, 0};
+      store_v(lv + 2 * D * BN);
+      load_tile(min(t0 + 1, t_end - 1)); store_v(lv + D * BN);
+      if (gt == 0) vscale[1] = sc_pend;
     }
-    // first staged loads of the loop: K(t0+1) by A, V(t0+2) by B
-    if (!group_b) { if (t0 + 1 < t_end) load_k(t0 + 1); }
-    else { if (t0 + 2 < t_end) load_v(t0 + 2); }
+    // first staged loads of the loop: K(t0+1) by A, V(t0+2) by B.  Tile
+    // indexes past the range are clamped to the last tile: the loop then
+    // stages harmless duplicates into free slots instead of branching.
+    const int tl = t_end - 1;
+    load_tile(min(t0 + 1 + (int)group_b, tl));
     lds_barrier();
     if (group_b) lds_barrier();            // group B runs one phase behind
 
-    bf16x8 pp[4];                          // P(t-1)
+    bf16x8 pp[4];                          // P(t-1); P(t0-1) = 0
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pp[c] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     int kslot = 0, vslot = 0;              // ring slots of tile t
     for (int t = t0; t < t_end; ++t) {
       const int vprev = vslot == 0 ? 2 : vslot - 1;
-      // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T
+      // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T,
+      // written as one software-pipelined stream: read j feeds MFMA j, and
+      // read j + NIF is issued right after MFMA j; scheduling barriers keep
+      // that order (the compiler would otherwise regroup the MFMAs and wait
+      // for every outstanding read).
       f32x16 s[2];
       {
-        const uint16_t* kl = lk + kslot * (BN * D);
+        uint32_t xk = kx ^ (uint32_t)(kslot * (BN * D * 2));
+        uint32_t xv = vx ^ (uint32_t)(vprev * (D * BN * 2));
+        asm volatile("" : "+v"(xk), "+v"(xv));   // per-tile values: keep the address math in the loop
+        const char* kbase = reinterpret_cast<const char*>(lk) + krow;
+        const char* vbase = reinterpret_cast<const char*>(lv) + vrow;
+        constexpr int NK = 2 * KK;               // K reads / S MFMAs
+        constexpr int NR = NK + 4 * DB;          // all reads (= MFMAs) of the phase
+        auto rd = [&](int j) -> bf16x8 {
+          if (j < NK) {
+            const int kk = j >> 1, mb = j & 1;
+            return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)(32 * kk)) ^ xk) + mb * 32 * D * 2));
+          }
+          const int c = (j - NK) / DB, db = (j - NK) % DB;
+          return __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
+        };
+        bf16x8 fr[NR];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          bf16x8 kf[2];
+        for (int j = 0; j < NIF; ++j) fr[j] = rd(j);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) kf[mb] = __builtin_bit_cast(bf16x8, ld16(kl + koff[kk] + mb * 32 * D));
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mb], qf[kk], kk == 0 ? f32x16{} : s[mb], 0, 0, 0);
+        for (int j = 0; j < NR; ++j) {
+          if (j < NK) {
+            const int kk = j >> 1, mb = j & 1;
+            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[kk], kk == 0 ? f32x16{} : s[mb], 0, 0, 0);
+          } else {
+            const int c = (j - NK) / DB, db = (j - NK) % DB;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
+          }
+          if (j + NIF < NR) fr[j + NIF] = rd(j + NIF);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // keep four LDS reads in flight ahead of the MFMAs that consume them
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * KK - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
-      if (t > t0) {
-        const uint16_t* vl = lv + vprev * (D * BN);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          bf16x8 vf[DB];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) vf[db] = __builtin_bit_cast(bf16x8, ld16(vl + voff[c] + db * 32 * BN));
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pp[c], o[db], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 4 * DB - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       const float ks = FP8 ? kscale[kslot] : 1.0f;
       const float vs = FP8 ? vscale[vslot] : 1.0f;
@@ -388,9 +398,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
-            acc += p;
-            if constexpr (FP8) p *= vs;
+            if constexpr (FP8) {
+              acc += p;
+              p *= vs;
+            }
             pp[c][e] = (__bf16)p;
+          }
+          if constexpr (!FP8) {
+            // row sum of the bf16 weights the PV product uses, two per dot2
+            const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pr = {pp[c][e], pp[c][e + 1]};
+              acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+            }
           }
           part[c] = acc;
         }
@@ -401,18 +422,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
       // staging: group A writes K(t+1) (slot kslot^1, which held K(t-1)) and
       // loads K(t+2); group B writes V(t+2) (slot of V(t-1)) and loads V(t+3)
       if (!group_b) {
-        if (t + 1 < t_end) {
-          store_k(lk + (kslot ^ 1) * (BN * D));
-          if (gt == 0) kscale[kslot ^ 1] = sc_pend;
-          if (t + 2 < t_end) load_k(t + 2);
-        }
+        store_k(lk + (kslot ^ 1) * (BN * D));
+        if (gt == 0) kscale[kslot ^ 1] = sc_pend;
       } else {
-        if (t + 2 < t_end) {
-          store_v(lv + vprev * (D * BN));
-          if (gt == 0) vscale[vprev] = sc_pend;
-          if (t + 3 < t_end) load_v(t + 3);
-        }
+        store_v(lv + vprev * (D * BN));
+        if (gt == 0) vscale[vprev] = sc_pend;
       }
+      load_tile(min(t + 2 + (int)group_b, tl));
       lds_barrier();
       kslot ^= 1;
       vslot = vslot == 2 ? 0 : vslot + 1;
@@ -420,12 +436,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
     // O += V(last)^T P(last)^T
     {
       const int vlast = vslot == 0 ? 2 : vslot - 1;
-      const uint16_t* vl = lv + vlast * (D * BN);
+      const uint32_t xv = vx ^ (uint32_t)(vlast * (D * BN * 2));
+      const char* vbase = reinterpret_cast<const char*>(lv) + vrow;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         bf16x8 vf[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vf[db] = __builtin_bit_cast(bf16x8, ld16(vl + voff[c] + db * 32 * BN));
+        for (int db = 0; db < DB; ++db)
+          vf[db] = __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pp[c], o[db], 0, 0, 0);

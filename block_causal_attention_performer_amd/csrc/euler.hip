@@ -12,8 +12,9 @@
 // as hi/lo bf16 rows per channel (w_prep_kernel, 64 bytes per row of W, into
 // the caller's workspace), so every MFMA operand is one 16-byte load.  The
 // main kernel is bound by reading x from HBM once: one workgroup per 16
-// tokens, its four waves split k and add their 16x16 partials through LDS
-// in a fixed order before the update.
+// tokens, its sixteen waves split k (many loads in flight per CU, since a
+// unit has only a few hundred such token groups) and add their 16x16
+// partials through LDS in a fixed order before the update.
 #include "bca_internal.h"
 
 namespace bca {
@@ -21,6 +22,7 @@ namespace bca {
 namespace {
 constexpr int kThreads = 256;
 constexpr int kTok = 16;       // tokens per workgroup
+constexpr int kProjWaves = 16; // waves per projection workgroup (split k)
 constexpr int kBatch = 8;      // k-steps loaded ahead per wave
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
@@ -41,13 +43,13 @@ __global__ __launch_bounds__(kThreads) void w_prep_kernel(const float* w, uint16
   wt_lo[(int64_t)c * k + kk] = bf16_rne(f - __uint_as_float((uint32_t)hi << 16));
 }
 
-__global__ __launch_bounds__(kThreads) void euler_proj_kernel(EulerArgs a) {
-  __shared__ float part[4][kTok * 16];
+__global__ __launch_bounds__(kProjWaves * 64) void euler_proj_kernel(EulerArgs a) {
+  __shared__ float part[kProjWaves][kTok * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = (int64_t)blockIdx.x * kTok + (lane & 15);
   const bool rv = row < a.n_tok;
   const int nsteps = a.k / 32;
-  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+  const int s0 = wave * nsteps / kProjWaves, s1 = (wave + 1) * nsteps / kProjWaves;
   const int oct = 8 * (lane >> 4);
   const uint16_t* xp = static_cast<const uint16_t*>(a.x) + row * a.k + oct;
   const uint16_t* hp = a.wt_hi + (int64_t)(lane & 15) * a.k + oct;
@@ -75,9 +77,12 @@ __global__ __launch_bounds__(kThreads) void euler_proj_kernel(EulerArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) part[wave][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
   __syncthreads();
+  if (tid >= kTok * 16) return;
   const int64_t tok = (int64_t)blockIdx.x * kTok + (tid >> 4);
   if (tok < a.n_tok) {
-    const float v = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kProjWaves; ++w) v += part[w][tid];
     float* zp = a.z + tok * 16 + (tid & 15);
     *zp = __builtin_fmaf(-a.dtau, v, *zp);
   }
@@ -133,7 +138,7 @@ hipError_t launch_w_prep(const float* w, uint16_t* wt_hi, uint16_t* wt_lo, int k
 
 hipError_t launch_euler_proj(const EulerArgs& a, hipStream_t s) {
   if (a.n_ch != 16 || a.k % 32 != 0 || !a.wt_hi || !a.wt_lo) return hipErrorInvalidValue;
-  euler_proj_kernel<<<(unsigned)((a.n_tok + kTok - 1) / kTok), kThreads, 0, s>>>(a);
+  euler_proj_kernel<<<(unsigned)((a.n_tok + kTok - 1) / kTok), kProjWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
