@@ -162,7 +162,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[hip.event() for _ in range(2 * S)] for _ in range(args.steps)]
+    evs = [[hip.event() for _ in range(3 * S)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -171,8 +171,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_unit = wall * 1e3 / args.steps
-    attn_ms = [hip.elapsed_ms(e[2 * s], e[2 * s + 1]) for e in evs for s in range(S)]
+    # main attention kernel (the roofline's kernel) and the whole call
+    # (with the split combine and the exact rerun of flagged tiles)
+    attn_ms = [hip.elapsed_ms(e[3 * s], e[3 * s + 1]) for e in evs for s in range(S)]
+    call_ms = [hip.elapsed_ms(e[3 * s], e[3 * s + 2]) for e in evs for s in range(S)]
     attn_avg = sum(attn_ms) / len(attn_ms)
+    call_avg = sum(call_ms) / len(call_ms)
     flops_call = w.attn_flops()
     attn_tflops = flops_call / (attn_avg * 1e-3) / 1e12
     value = S * flops_call / (ms_unit * 1e-3) / 1e12
@@ -181,7 +185,7 @@ def main():
     # the caches are flushed by READING a 1 GiB buffer: a write flush would
     # leave dirty lines in the 256 MB last-level cache whose write-back then
     # lands inside the timed kernel.
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # float sum: no widening copy
     e0, e1 = hip.event(), hip.event()
     app_ms, eul_ms = [], []
     for _ in range(args.kernel_reps):
@@ -228,10 +232,12 @@ def main():
         "units_per_s": round(1e3 / ms_unit, 2),
         "unit_budget_frac": round(ms_unit / UNIT_BUDGET_MS, 4),
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "attn_call_ms": round(call_avg, 4),
+        "attn_call_tflops": round(flops_call / (call_avg * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(), "kernel": "attn_mfma_kernel",
+                     "traffic": _traffic(), "kernel": "attn_fwd_kernel<128>",
                      "avg_launch_ms": round(attn_avg, 4), "flops_per_launch": flops_call},
         "kernels": {
             "kv_append": {"median_ms": round(app_med, 5), "bytes": app_bytes,

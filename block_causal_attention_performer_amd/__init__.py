@@ -214,6 +214,8 @@ def performer_unit(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: 
         o_scratch = torch.empty(q.shape, dtype=cache.compute_dtype, device=q.device)
     ev = None
     if attn_events is not None:
+        if len(attn_events) != 3 * n_steps:
+            raise ValueError("attn_events needs 3 events per solver step")
         ev = (ctypes.c_void_p * len(attn_events))(*attn_events)
     st = lib().performer_unit(
         ctypes.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), q.shape[0], _ptr(w), _ptr(z),

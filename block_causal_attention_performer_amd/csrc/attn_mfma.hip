@@ -551,12 +551,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 namespace {
 template <int D, bool FP8, bool SMALL>
-hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_t(const AttnArgs& a, hipEvent_t main_done, hipStream_t s) {
   const int64_t nqt = (a.n_q + BM - 1) / BM;
   const int64_t total = nqt * a.n_heads * a.nsplit;
   const unsigned grid = (unsigned)((total + 7) / 8 * 8);
   attn_fwd_kernel<D, FP8, SMALL><<<grid, NT, 0, s>>>(a);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && main_done) e = hipEventRecord(main_done, s);
   if (e != hipSuccess || a.nsplit == 1) return e;
   const unsigned cgrid = (unsigned)((a.n_q * a.n_heads + 3) / 4);
   attn_combine_kernel<D><<<cgrid, 256, 0, s>>>(a);
@@ -566,15 +567,15 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 
 int attn_mfma_rows_per_wg() { return BM; }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s) {
+hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done, hipStream_t s) {
   const bool small = a.ps_log2 < 6;
   if (kv_fp8) {
     if (a.head_dim != 128 || small) return hipErrorInvalidValue;
-    return launch_t<128, true, false>(a, s);
+    return launch_t<128, true, false>(a, main_done, s);
   }
   switch (a.head_dim) {
-    case 64: return small ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s);
-    case 128: return small ? launch_t<128, false, true>(a, s) : launch_t<128, false, false>(a, s);
+    case 64: return small ? launch_t<64, false, true>(a, main_done, s) : launch_t<64, false, false>(a, main_done, s);
+    case 128: return small ? launch_t<128, false, true>(a, main_done, s) : launch_t<128, false, false>(a, main_done, s);
     default: return hipErrorInvalidValue;
   }
 }

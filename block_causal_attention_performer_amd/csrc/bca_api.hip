@@ -158,7 +158,7 @@ bca_status check_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t block_
 bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t block_size,
                         const bca_kv_cache* c, int64_t n_kv, void* out, int32_t out_dtype,
                         float softmax_scale, void* workspace, size_t workspace_bytes,
-                        hipStream_t s) {
+                        hipEvent_t main_done, hipStream_t s) {
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)c->head_dim);
   AttnArgs a{};
   a.q = q;
@@ -184,6 +184,7 @@ bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t bloc
   if (c->dtype == BCA_F32) {
     a.nsplit = 1;
     e = launch_attn_f32(a, s);
+    if (e == hipSuccess && main_done) e = hipEventRecord(main_done, s);
   } else if (room >= attn_split_bytes(c, n_q, 1)) {
     // fast kernel (+ combine), then the exact kernel for flagged query tiles
     a.nsplit = choose_attn_split(c, n_q, q_pos0, block_size, n_kv, room);
@@ -195,7 +196,7 @@ bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t bloc
       a.ws_o = reinterpret_cast<float*>(ws);
       a.ws_ml = reinterpret_cast<float*>(ws + align256(per * c->head_dim * 4));
     }
-    e = launch_attn_mfma(a, fp8, s);
+    e = launch_attn_mfma(a, fp8, main_done, s);
     if (e == hipSuccess) {
       AttnArgs x = a;
       x.flags = a.flags_out;
@@ -207,6 +208,7 @@ bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t bloc
   } else {
     a.nsplit = 1;
     e = launch_attn_exact(a, fp8, s);
+    if (e == hipSuccess && main_done) e = hipEventRecord(main_done, s);
   }
   return e == hipSuccess ? BCA_OK : BCA_EHIP;
 }
@@ -301,7 +303,7 @@ bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t
     if (room > skip) { ws += skip; room -= skip; } else { ws = nullptr; room = 0; }
   }
   return enqueue_attn(q, n_q, q_pos0, block_size, c, n_kv, out, out_dtype, softmax_scale, ws,
-                      room, s);
+                      room, nullptr, s);
 }
 
 bca_status fm_euler_step(float* z, const void* x, const float* w, int64_t n_tok, int32_t k,
@@ -347,11 +349,12 @@ bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new,
   char* attn_ws = room > wt_bytes ? ws + wt_bytes : nullptr;
   const size_t attn_room = room > wt_bytes ? room - wt_bytes : 0;
   for (int32_t step = 0; step < n_steps; ++step) {
-    if (attn_events && hipEventRecord(attn_events[2 * step], s) != hipSuccess) return BCA_EHIP;
+    hipEvent_t* ev = attn_events ? attn_events + 3 * step : nullptr;
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return BCA_EHIP;
     st = enqueue_attn(q, n_q, n_kv - n_q, (int32_t)n_q, c, n_kv, o_scratch, io, 0.0f, attn_ws,
-                      attn_room, s);
+                      attn_room, ev ? ev[1] : nullptr, s);
     if (st != BCA_OK) return st;
-    if (attn_events && hipEventRecord(attn_events[2 * step + 1], s) != hipSuccess) return BCA_EHIP;
+    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return BCA_EHIP;
     st = enqueue_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io, wt ? ws : nullptr,
                        wt ? wt_bytes : 0, wt, s);
     if (st != BCA_OK) return st;

@@ -63,7 +63,9 @@ struct AttnArgs {
 };
 // bf16 / fp8 MFMA path.  kv_fp8 selects fp8 pages.  Returns the error of the
 // launch; nsplit > 1 also launches the combine.  Needs flags_out.
-hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s);
+// main_done (may be null) is recorded on s after the main kernel, before
+// the split combine
+hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done, hipStream_t s);
 // Exact-rescaling MFMA kernel (no split); with flags set it only rewrites
 // flagged query tiles.
 hipError_t launch_attn_exact(const AttnArgs& a, bool kv_fp8, hipStream_t s);

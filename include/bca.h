@@ -184,8 +184,11 @@ BCA_API bca_status fm_euler_step(float* z, const void* x, const float* w,
  *   o_scratch: [n_q][n_heads][head_dim] (f32 for an f32 cache, else bf16)
  *   workspace: as for block_causal_attn / fm_euler_step (may be NULL);
  *       bca_workspace_bytes() gives the size for the fastest path
- *   attn_events: NULL, or 2*n_steps events; event 2s is recorded on s just
- *       before attention step s and event 2s+1 just after it (timing hook)
+ *   attn_events: NULL, or 3*n_steps events (timing hook): for step s,
+ *       event 3s is recorded on the stream just before its attention,
+ *       3s+1 right after the main attention kernel (before the split
+ *       combine and the exact rerun of flagged tiles) and 3s+2 after the
+ *       whole attention call
  * All arguments of all four phases are validated before the first launch.
  */
 BCA_API bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new,

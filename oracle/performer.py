@@ -263,16 +263,20 @@ class PagedCacheFP8:
         self.n_tokens = n0 + n
 
     def gather(self, n: Optional[int] = None):
-        """Dequantised K, V [n, H, D] float64: decode(code) * scale."""
+        """Dequantised K, V [n, H, D] float64: decode(code) * scale, page by
+        page (logical page lp holds tokens lp*ps .. lp*ps + ps - 1)."""
         n = self.n_tokens if n is None else n
         K = np.zeros((n, self.H, self.D))
         V = np.zeros((n, self.H, self.D))
-        for t in range(n):
-            page, slot = self.pt[t // self.ps], t % self.ps
-            K[t] = e4m3_decode(self.k_codes[page, :, slot, :]) * \
-                self.k_scales[page][:, None].astype(np.float64)
-            V[t] = e4m3_decode(self.v_codes[page, :, :, slot]) * \
-                self.v_scales[page][:, None].astype(np.float64)
+        for lp in range(-(-n // self.ps)):
+            t0, t1 = lp * self.ps, min(n, (lp + 1) * self.ps)
+            page = self.pt[lp]
+            ks = self.k_scales[page].astype(np.float64)[:, None, None]   # [H,1,1]
+            vs = self.v_scales[page].astype(np.float64)[:, None, None]
+            kd = e4m3_decode(self.k_codes[page, :, : t1 - t0, :]) * ks   # [H, rows, D]
+            vd = e4m3_decode(self.v_codes[page, :, :, : t1 - t0]) * vs   # [H, D, rows]
+            K[t0:t1] = kd.transpose(1, 0, 2)
+            V[t0:t1] = vd.transpose(2, 0, 1)
         return K, V
 
 

@@ -258,6 +258,34 @@ def test_fp8_cache_rows_past_valid_are_zero():
         c.append(_rand(4, H, D), _rand(4, H, D))
 
 
+def test_fp8_cache_gather_is_identity_on_the_grid():
+    """Values on the E4M3 grid with each page's amax = 448 have scale 1 and
+    inv 1 exactly, so append + gather returns them unchanged: a transposed
+    V block, a wrong page or slot, or a dropped scale shows up as a
+    mismatch.  Pages are shuffled and the last page is partial."""
+    H, D, ps = 3, 8, 16
+    rng = np.random.default_rng(7)
+    n = 3 * ps + 5
+    grid = oracle.e4m3_decode(np.arange(0x7F))           # 0 .. 448
+    k = rng.choice(grid, size=(n, H, D)) * rng.choice([-1.0, 1.0], size=(n, H, D))
+    v = rng.choice(grid, size=(n, H, D)) * rng.choice([-1.0, 1.0], size=(n, H, D))
+    for t0 in range(0, n, ps):                            # amax 448 in every page and head
+        k[t0, :, 0] = 448.0
+        v[t0, :, 1] = -448.0
+    c = oracle.PagedCacheFP8(H, D, ps, [2, 0, 3, 1], 4)
+    c.append(k.astype(np.float32), v.astype(np.float32))
+    assert np.all(c.k_scales[[2, 0, 3, 1]] == 1.0) and np.all(c.v_scales[[2, 0, 3, 1]] == 1.0)
+    K, V = c.gather()
+    np.testing.assert_array_equal(K, k)
+    np.testing.assert_array_equal(V, v)
+    # a non-unit scale multiplies back: halve every value, scale 0.5
+    c2 = oracle.PagedCacheFP8(H, D, ps, [1, 3, 0, 2], 4)
+    c2.append((k / 2).astype(np.float32), (v / 2).astype(np.float32))
+    K2, V2 = c2.gather()
+    np.testing.assert_array_equal(K2, k / 2)
+    np.testing.assert_array_equal(V2, v / 2)
+
+
 # ---------------------------------------------------------------- velocity / Euler
 
 

@@ -20,7 +20,10 @@ alwayszhang.cn deep read, section 3.3):
 Draw recipe: every tensor has its own sub-stream, seed = 1000*cfg_index +
 slot, slots in the order Q, K_hist, V_hist, K_new, V_new, eps, z0, W.
 Q/K/V ~ scale * N(0,1) drawn in fp32 and rounded to nearest-even bf16 where
-the workload is bf16; eps, z0, W ~ N(0,1) fp32.
+the workload is bf16; eps, z0, W ~ N(0,1) fp32.  The long fp8 history is
+drawn in chunks of two units (a whole number of 256-token pages), chunk c of
+slot K_hist / V_hist from seed (1000*cfg_index + slot) * 100000 + c + 1, as
+bf16 sources that the cache quantises on append.
 """
 from __future__ import annotations
 
@@ -147,3 +150,23 @@ def peaky(t: torch.Tensor, factor: float) -> torch.Tensor:
     """Scale a bf16/f32 tensor by an exact power of two (keeps values
     representable), used for the sharp-softmax variants."""
     return (t.float() * factor).to(t.dtype)
+
+
+def hist_chunk_tokens(w: Workload) -> int:
+    """Tokens per history chunk: two units (7424 at v0.2 = 29 pages)."""
+    return 2 * w.unit_tokens
+
+
+def hist_chunk(w: Workload, slot: str, c: int, device="cpu") -> torch.Tensor:
+    """History chunk c ([hist_chunk_tokens, H, D] bf16) of K_hist or V_hist."""
+    if slot not in ("k_hist", "v_hist"):
+        raise ValueError(slot)
+    n = hist_chunk_tokens(w)
+    if (c + 1) * n > w.n_hist:
+        raise ValueError("chunk past the history")
+    seed = seed_for(w.index, slot) * 100000 + c + 1
+    return qkv(seed, n, w.n_heads, w.head_dim, w.qkv_scale, "bf16", device)
+
+
+def n_hist_chunks(w: Workload) -> int:
+    return w.n_hist // hist_chunk_tokens(w)
