@@ -1,0 +1,416 @@
+// Block-causal attention over the paged KV cache: bf16 MFMA kernel whose
+// K / V^T tiles move HBM -> LDS by direct 16-byte LDS loads (gfx950
+// global_load_lds_dwordx4), head dim 128, pages of >= 64 keys.
+//
+// Visibility (explainer "wan-streamer-realtime-av", listening-while-speaking
+// section and its figure caption; youleyou.com article section 3.1): query
+// at global position p sees key j iff j / B <= p / B.
+//
+// Compute is that of the register-staged kernel (attn_mfma.hip): one
+// workgroup = 8 waves x 32 query rows of one head, two wave groups one
+// barrier apart so one group's MFMAs (S(t) = K(t) Q^T, O += V(t-1)^T
+// P(t-1)^T) overlap the other's softmax; the fixed-reference base-2 softmax
+// with an overflow flag and the exact kernel as fallback; split partials.
+//
+// Staging: group A streams K tiles, group B V^T tiles, two tiles ahead,
+// straight into LDS.  A direct LDS load writes lane i's 16 bytes at
+// (wave-uniform base) + 16 i, so each lane fetches the global chunk that
+// the XOR-swizzled LDS layout wants at its position.  Three slots per ring
+// (the tile being read, the next one, the one in flight), each a separate
+// LDS array and the loop unrolled by three, so every slot is named at
+// compile time: reads of one slot never wait for loads into another.  A
+// group waits for its own previous tile (vmcnt) before the barrier that
+// publishes it.  V values of keys past n_kv are zeroed in LDS after they
+// land (tail tile only).
+#include <math.h>
+
+#include <type_traits>
+
+#include "attn_common.h"
+
+namespace bca {
+namespace {
+
+using namespace attn;
+
+constexpr int BN = kKeyTile;      // keys per tile
+constexpr int QW = 32;            // query rows per wave
+constexpr int NW = 8;             // waves per workgroup (two groups of four)
+constexpr int NT = NW * 64;
+constexpr int GT = NT / 2;        // threads per group
+constexpr int BM = NW * QW;       // query rows per workgroup
+constexpr int NIF = 4;            // LDS reads kept in flight ahead of the MFMAs
+static_assert(NW == kAttnFlagWaves, "one overflow flag per wave");
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef const __attribute__((address_space(1))) void* gbl_ptr;
+
+// s_waitcnt with only vmcnt = n (lgkmcnt and expcnt left alone)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
+  constexpr int KK = D / 16;                 // k-steps of S^T
+  constexpr int DB = D / 32;                 // head-dim blocks of O^T
+  constexpr int RK = D / 8;                  // 16-byte chunks per LDS K row
+  constexpr int SLOT = BN * D * 2;           // bytes per K or V^T slot
+  constexpr int NL = SLOT / (GT * 16);       // direct loads per thread per tile
+  static_assert(NL == 4 && RK == 16, "staging layout assumes D = 128");
+
+  __shared__ __attribute__((aligned(1024))) char lk0[SLOT], lk1[SLOT], lk2[SLOT];
+  __shared__ __attribute__((aligned(1024))) char lv0[SLOT], lv1[SLOT], lv2[SLOT];
+  auto kslot = [&](auto r) -> char* {
+    if constexpr (decltype(r)::value == 0) return lk0;
+    else if constexpr (decltype(r)::value == 1) return lk1;
+    else return lk2;
+  };
+  auto vslot = [&](auto r) -> char* {
+    if constexpr (decltype(r)::value == 0) return lv0;
+    else if constexpr (decltype(r)::value == 1) return lv1;
+    else return lv2;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_b = wave >= NW / 2;
+  const int gw = wave & 3;                   // wave index inside its group
+
+  // XCD-aware mapping (consecutive block ids go to the 8 XCDs in turn).
+  const int G = gridDim.x;
+  const int lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int H = a.n_heads;
+  const int nqt = (int)((a.n_q + BM - 1) / BM);
+  if (lid >= nqt * H * a.nsplit) return;
+  const int qt = lid % nqt;
+  const int rest = lid / nqt;
+  const int split = rest % a.nsplit;
+  const int h = rest / a.nsplit;
+
+  const int64_t B = a.block_size;
+  const int64_t r0 = (int64_t)qt * BM;
+  const int64_t rlast = (r0 + BM < a.n_q ? r0 + BM : a.n_q) - 1;
+  const int64_t lim_first = min(a.n_kv, ((a.q_pos0 + r0) / B + 1) * B);
+  const int64_t lim_last = min(a.n_kv, ((a.q_pos0 + rlast) / B + 1) * B);
+  const int ntile = (int)((lim_last + BN - 1) / BN);
+  const int t_begin = (int)((int64_t)split * ntile / a.nsplit);
+  const int t_end = (int)((int64_t)(split + 1) * ntile / a.nsplit);
+
+  const int64_t qrow = r0 + wave * QW + col;
+  const int64_t lim = min(a.n_kv, ((a.q_pos0 + qrow) / B + 1) * B);
+
+  bf16x8 qf[KK];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow * H + h) * D + 8 * half;
+    const bool ok = qrow < a.n_q;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(qp + 16 * kk) : u32x4{0, 0, 0, 0});
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  bool overflow = false;
+
+  // per-lane LDS read addresses: chunk j of the lane's row at row + ((16 j) ^ x)
+  const int kr = sigma32(col);
+  const uint32_t krow = (uint32_t)(kr * D * 2), kx = (uint32_t)((swz<RK>(kr) ^ half) * 16);
+  const uint32_t vrow = (uint32_t)(kr * BN * 2), vx = (uint32_t)((swz<8>(kr) ^ half) * 16);
+
+  const int ps_log2 = a.ps_log2;
+  const int psm = (1 << ps_log2) - 1;
+  const char* kpages = static_cast<const char*>(a.k_pages);
+  const char* vpages = static_cast<const char*>(a.v_pages);
+
+  // ------------------------------------------------------------ staging
+  // Direct load i of wave gw writes LDS bytes [i*4096 + gw*1024, +1024) of
+  // the slot.  K: 4 rows of 256 bytes, lane -> row 16i + 4gw + lane/16,
+  // position lane%16, global chunk position ^ swz16(row).  V^T: 8 rows of
+  // 128 bytes, lane -> head dim 32i + 8gw + lane/8, position lane%8, global
+  // chunk position ^ swz8(d).  The swizzles depend on the row's low 4 bits
+  // only, so load i is the lane offset of load 0 plus a uniform step.
+  uint32_t goff;
+  int64_t gstep;
+  if (!group_b) {
+    const int row = 4 * gw + (lane >> 4);
+    goff = (uint32_t)(row * 256 + (((lane & 15) ^ swz<16>(row)) * 16));
+    gstep = 16 * 256;
+  } else {
+    const int d = 8 * gw + (lane >> 3);
+    goff = (uint32_t)(((int64_t)d << ps_log2) * 2 + (((lane & 7) ^ swz<8>(d)) * 16));
+    gstep = (int64_t)32 << ps_log2 << 1;
+  }
+  // issue the direct loads of tile t (K for group A, V^T for group B) into `dst`
+  auto stage = [&](int t, char* dst) {
+    const int64_t k0 = (int64_t)t * BN;
+    const int64_t page = page_of(a.page_table, k0 >> ps_log2);
+    const int64_t ph = page * H + h;
+    const char* base = group_b ? vpages + (((ph * D) << ps_log2) + (k0 & psm)) * 2
+                               : kpages + ((((ph << ps_log2) | (k0 & psm)) * D) * 2);
+    char* l = dst + gw * 1024;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr)(base + i * gstep + goff), (lds_ptr)(l + i * 4096), 16, 0, 0);
+  };
+  // group B, tail tile: zero the V^T entries of keys >= n_kv once they
+  // landed.  Chunk position c of head-dim row d holds the keys
+  // (c ^ swz8(d)) * 8 .. +7; each thread rewrites 4 of the 1024 chunks.
+  auto zero_tail = [&](int t, char* vl) {
+    const int64_t k0 = (int64_t)t * BN;
+    if (k0 + BN <= a.n_kv) return;
+    wait_vm<0>();
+    const int nvalid = (int)(a.n_kv - k0);   // keys of the tile that exist
+    const int gt = tid & (GT - 1);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = i * GT + gt;             // chunk index: row q / 8, position q % 8
+      const int d = q >> 3, c = q & 7;
+      const int key0 = (c ^ swz<8>(d)) * 8;
+      u32x4* p = reinterpret_cast<u32x4*>(vl + q * 16);
+      u32x4 v = *p;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (key0 + 2 * w >= nvalid) v[w] &= 0xFFFF0000u;
+        if (key0 + 2 * w + 1 >= nvalid) v[w] &= 0x0000FFFFu;
+      }
+      *p = v;
+    }
+  };
+
+  // ------------------------------------------------------------ main loop
+  if (t_begin < t_end) {
+    const int t0 = t_begin, tl = t_end - 1;
+    // prologue: K(t0), K(t0+1) into K slots 0, 1 (group A); V(t0), V(t0+1)
+    // into V slots 0, 1 and zeros into V slot 2, which stands for V(t0-1)
+    // (group B); P(t0-1) = 0, so the first PV step adds exact zeros.
+    if (!group_b) {
+      stage(t0, lk0);
+      stage(min(t0 + 1, tl), lk1);
+    } else {
+      stage(t0, lv0);
+      stage(min(t0 + 1, tl), lv1);
+      const int gt = tid & (GT - 1);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lv2 + (i * GT + gt) * 16) = u32x4{0, 0, 0, 0};
+      wait_vm<0>();
+      zero_tail(t0, lv0);
+      zero_tail(min(t0 + 1, tl), lv1);
+    }
+    wait_vm<0>();
+    lds_barrier();
+    if (group_b) lds_barrier();            // group B runs one phase behind
+
+    bf16x8 pp[4];                          // P(t-1); P(t0-1) = 0
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pp[c] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+
+    // iteration t with ring position R = (t - t0) % 3: K(t) and V(t) in
+    // slot R, V(t-1) in slot R+2 (mod 3), which also receives K(t+2) and
+    // V(t+2) during the vector phase
+    auto iter = [&](int t, auto R) {
+      constexpr int r = decltype(R)::value;
+      constexpr int rp = (r + 2) % 3;
+      char* kl = kslot(ic<r>{});
+      char* vprev = vslot(ic<rp>{});
+      // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T
+      f32x16 s[2];
+      {
+        // opaque per-iteration copies: keep the read addresses from being
+        // precomputed for all three slots outside the loop
+        uint32_t xk = kx, xv = vx, kro = krow, vro = vrow;
+        asm volatile("" : "+v"(xk), "+v"(xv), "+v"(kro), "+v"(vro));
+        const char* kbase = kl + kro;
+        const char* vbase = vprev + vro;
+        constexpr int NK = 2 * KK;
+        constexpr int NR = NK + 4 * DB;
+        auto rd = [&](int j) -> bf16x8 {
+          if (j < NK) {
+            const int kk = j >> 1, mb = j & 1;
+            return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)(32 * kk)) ^ xk) + mb * 32 * D * 2));
+          }
+          const int c = (j - NK) / DB, db = (j - NK) % DB;
+          return __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
+        };
+        bf16x8 fr[NR];
+#pragma unroll
+        for (int j = 0; j < NIF; ++j) fr[j] = rd(j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+          if (j < NK) {
+            const int kk = j >> 1, mb = j & 1;
+            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[kk], kk == 0 ? f32x16{} : s[mb], 0, 0, 0);
+          } else {
+            const int c = (j - NK) / DB, db = (j - NK) % DB;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
+          }
+          if (j + NIF < NR) fr[j + NIF] = rd(j + NIF);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      lds_barrier();
+
+      // ---------------- vector phase: next tile two ahead into the free
+      // slot, then the softmax of tile t -> P(t)
+      const int tn = min(t + 2, tl);
+      if (!group_b) stage(tn, kslot(ic<rp>{}));
+      else stage(tn, vslot(ic<rp>{}));
+      {
+        const int64_t k0 = (int64_t)t * BN;
+        if (k0 + BN > lim_first) {
+          const int lrel = (int)min(lim - k0, (int64_t)BN);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const int key = 32 * mb + 16 * (rr >> 3) + 8 * half + (rr & 7);
+              if (key >= lrel) s[mb][rr] = -INFINITY;
+            }
+        }
+        const float sl = a.scale_log2;
+        if (t == t0) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+          m_run = pair_max(mx) * sl;
+        }
+        const float mneg = -m_run;
+        float part[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int mb = c >> 1, rb = 8 * (c & 1);
+          float acc = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
+            acc += p;
+            pp[c][e] = (__bf16)p;
+          }
+          part[c] = acc;
+        }
+        const float tsum = (part[0] + part[1]) + (part[2] + part[3]);
+        overflow |= !(tsum <= kSlowSum);
+        l_run += tsum;
+      }
+      // publish the tile staged one iteration ago (t+1): wait for its loads
+      // (the NL just issued may stay in flight); group B clears its tail
+      wait_vm<NL>();
+      if (group_b) zero_tail(min(t + 1, tl), vslot(ic<(r + 1) % 3>{}));
+      lds_barrier();
+    };
+
+    int t = t0;
+    for (; t + 2 <= tl; t += 3) {
+      iter(t, ic<0>{});
+      iter(t + 1, ic<1>{});
+      iter(t + 2, ic<2>{});
+    }
+    if (t <= tl) iter(t, ic<0>{});
+    if (t + 1 <= tl) iter(t + 1, ic<1>{});
+    // O += V(last)^T P(last)^T: V(tl) sits in slot (tl - t0) % 3
+    {
+      const int rl = (tl - t0) % 3;
+      const char* vl = rl == 0 ? lv0 : (rl == 1 ? lv1 : lv2);
+      const char* vbase = vl + vrow;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x8 vf[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          vf[db] = __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ vx) + db * 32 * BN * 2));
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pp[c], o[db], 0, 0, 0);
+      }
+    }
+    if (!group_b) lds_barrier();           // balance group B's extra barrier
+    wait_vm<0>();                          // no direct load outlives the workgroup
+  }
+
+  // one flag per (query tile, split, wave), written unconditionally
+  const bool wave_overflow = __builtin_amdgcn_ballot_w64(overflow) != 0;
+  if (lane == 0) a.flags_out[((int64_t)(h * nqt + qt) * a.nsplit + split) * NW + wave] = wave_overflow;
+  if (wave_overflow) {
+    m_run = 0.0f;
+    l_run = 1.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  }
+
+  // ---------------- epilogue: lane owns query `col` and head dims
+  // 32*db + 8*half + [0,8) (regs 0..7) and +16 (regs 8..15).
+  const float l_tot = pair_sum(l_run);
+  if (qrow >= a.n_q) return;
+  if (a.nsplit == 1) {
+    const float inv = 1.0f / l_tot;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int run = 0; run < 2; ++run) {
+        const int d = 32 * db + 16 * run + 8 * half;
+        const int64_t off = (qrow * H + h) * D + d;
+        if (a.out_f32) {
+          float* op = static_cast<float*>(a.out) + off;
+          f32x4 x0, x1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x0[e] = o[db][8 * run + e] * inv;
+            x1[e] = o[db][8 * run + 4 + e] * inv;
+          }
+          *reinterpret_cast<f32x4*>(op) = x0;
+          *reinterpret_cast<f32x4*>(op + 4) = x1;
+        } else {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)(o[db][8 * run + e] * inv);
+          *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(a.out) + off) = v;
+        }
+      }
+  } else {
+    const int64_t prow = (int64_t)split * a.n_q + qrow;
+    float* op = a.ws_o + (prow * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int run = 0; run < 2; ++run) {
+        const int d = 32 * db + 16 * run + 8 * half;
+        f32x4 x0, x1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x0[e] = o[db][8 * run + e];
+          x1[e] = o[db][8 * run + 4 + e];
+        }
+        *reinterpret_cast<f32x4*>(op + d) = x0;
+        *reinterpret_cast<f32x4*>(op + d + 4) = x1;
+      }
+    if (half == 0) {
+      float* ml = a.ws_ml + (prow * H + h) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+  }
+}
+
+hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t s) {
+  if (a.head_dim != 128 || a.ps_log2 < 6) return hipErrorInvalidValue;
+  const int64_t nqt = (a.n_q + BM - 1) / BM;
+  const int64_t total = nqt * a.n_heads * a.nsplit;
+  const unsigned grid = (unsigned)((total + 7) / 8 * 8);
+  attn_dma_kernel<128><<<grid, NT, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace bca

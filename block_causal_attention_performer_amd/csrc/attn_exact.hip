@@ -32,48 +32,15 @@
 //   combine.
 #include <math.h>
 
-#include "bca_internal.h"
+#include "attn_common.h"
 
 namespace bca {
 namespace {
 
+using namespace attn;
+
 constexpr int BN = kKeyTile;
 constexpr float kRescaleLog2 = 8.0f;
-
-__device__ __forceinline__ int sigma32(int m) {
-  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
-}
-
-// 16-byte chunk swizzle for LDS rows of R chunks (R = 8 or 16).
-template <int R>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (R == 16) {
-    return (row & 3) | ((row >> 1) & 4) | ((row << 1) & 8);
-  } else {
-    return ((row >> 1) & 1) | ((row >> 2) & 2) | (((row ^ (row >> 2)) & 1) << 2);
-  }
-}
-
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// fp8 E4M3FN -> bf16 bits for 4 codes packed in a u32 (two bf16 pairs).  The
-// conversion is exact (3 mantissa bits fit in bf16's 7).
-__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  uint32_t a = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-  uint32_t b = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
-  return make_uint2(a, b);
-}
 
 template <int D, int NT, bool FP8>
 struct TileLoader {

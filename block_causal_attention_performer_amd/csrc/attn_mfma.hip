@@ -38,10 +38,12 @@
 // unnormalised partials merged by a fixed-order log-sum-exp combine.
 #include <math.h>
 
-#include "bca_internal.h"
+#include "attn_common.h"
 
 namespace bca {
 namespace {
+
+using namespace attn;
 
 constexpr int BN = kKeyTile;      // keys per tile
 constexpr int QW = 32;            // query rows per wave
@@ -53,63 +55,7 @@ constexpr int BM = NW * QW;       // query rows per workgroup
 #define BCA_ATTN_NIF 6
 #endif
 constexpr int NIF = BCA_ATTN_NIF; // LDS reads kept in flight ahead of the MFMAs
-constexpr float kSlowSum = 1099511627776.0f;   // 2^40
 static_assert(NW == kAttnFlagWaves, "one overflow flag per wave");
-
-__device__ __forceinline__ int sigma32(int m) {
-  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
-}
-
-// 16-byte chunk swizzle for LDS rows of R chunks (R = 8 or 16): the 8 (or
-// 16) rows read by one group of lanes land in distinct banks.
-template <int R>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (R == 16) {
-    return (row & 3) | ((row >> 1) & 4) | ((row << 1) & 8);
-  } else {
-    return ((row >> 1) & 1) | ((row >> 2) & 2) | (((row ^ (row >> 2)) & 1) << 2);
-  }
-}
-
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// Page-table entry through the scalar cache: the table is read-only for the
-// whole launch and the index is uniform, so the physical page (and every
-// tile base address derived from it) lives in scalar registers.
-__device__ __forceinline__ int64_t page_of(const int32_t* pt, int64_t lp) {
-  return ((const __attribute__((address_space(4))) int32_t*)(const void*)pt)[lp];
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// fp8 E4M3FN -> bf16 bits for 4 codes packed in a u32.  Exact (3 mantissa
-// bits fit in bf16's 7; the E4M3 exponent range fits bf16's).
-__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  uint32_t a = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-  uint32_t b = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
-  return make_uint2(a, b);
-}
-
-// Workgroup barrier that waits only for this wave's LDS traffic, not for
-// global loads still in flight (they land in registers and are waited for
-// at their use).  The asm clobber keeps the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unchanged
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 }  // namespace
 
@@ -366,7 +312,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
       const float vs = FP8 ? vscale[vslot] : 1.0f;
       lds_barrier();
 
-      // ---------------- vector phase: softmax of tile t -> P(t)
+      // ---------------- vector phase
+      // staging first, so the LDS writes and the next loads overlap the
+      // softmax: group A writes K(t+1) (slot kslot^1, which held K(t-1):
+      // both groups read it before this phase) and loads K(t+2); group B
+      // writes V(t+2) (slot of V(t-1)) and loads V(t+3)
+      if (!group_b) {
+        store_k(lk + (kslot ^ 1) * (BN * D));
+        if (gt == 0) kscale[kslot ^ 1] = sc_pend;
+      } else {
+        store_v(lv + vprev * (D * BN));
+        if (gt == 0) vscale[vprev] = sc_pend;
+      }
+      load_tile(min(t + 2 + (int)group_b, tl));
+      // softmax of tile t -> P(t)
       {
         const int64_t k0 = (int64_t)t * BN;
         if (k0 + BN > lim_first) {
@@ -394,24 +353,15 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int mb = c >> 1, rb = 8 * (c & 1);
+          // fp32 adds (v_dot2 would share the matrix pipe with the other
+          // group's MFMAs)
           float acc = 0.0f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
-            if constexpr (FP8) {
-              acc += p;
-              p *= vs;
-            }
+            acc += p;
+            if constexpr (FP8) p *= vs;
             pp[c][e] = (__bf16)p;
-          }
-          if constexpr (!FP8) {
-            // row sum of the bf16 weights the PV product uses, two per dot2
-            const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const bf16x2 pr = {pp[c][e], pp[c][e + 1]};
-              acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
-            }
           }
           part[c] = acc;
         }
@@ -419,16 +369,6 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
         overflow |= !(tsum <= kSlowSum);
         l_run += tsum;
       }
-      // staging: group A writes K(t+1) (slot kslot^1, which held K(t-1)) and
-      // loads K(t+2); group B writes V(t+2) (slot of V(t-1)) and loads V(t+3)
-      if (!group_b) {
-        store_k(lk + (kslot ^ 1) * (BN * D));
-        if (gt == 0) kscale[kslot ^ 1] = sc_pend;
-      } else {
-        store_v(lv + vprev * (D * BN));
-        if (gt == 0) vscale[vprev] = sc_pend;
-      }
-      load_tile(min(t + 2 + (int)group_b, tl));
       lds_barrier();
       kslot ^= 1;
       vslot = vslot == 2 ? 0 : vslot + 1;
@@ -549,18 +489,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+#ifndef BCA_ATTN_WIDE
+#define BCA_ATTN_WIDE 0
+#endif
+#ifndef BCA_ATTN_DMA
+#define BCA_ATTN_DMA 1
+#endif
+
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
+  const unsigned cgrid = (unsigned)((a.n_q * a.n_heads + 3) / 4);
+  switch (a.head_dim) {
+    case 64: attn_combine_kernel<64><<<cgrid, 256, 0, s>>>(a); break;
+    case 128: attn_combine_kernel<128><<<cgrid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 namespace {
 template <int D, bool FP8, bool SMALL>
-hipError_t launch_t(const AttnArgs& a, hipEvent_t main_done, hipStream_t s) {
+hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int64_t nqt = (a.n_q + BM - 1) / BM;
   const int64_t total = nqt * a.n_heads * a.nsplit;
   const unsigned grid = (unsigned)((total + 7) / 8 * 8);
   attn_fwd_kernel<D, FP8, SMALL><<<grid, NT, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && main_done) e = hipEventRecord(main_done, s);
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  const unsigned cgrid = (unsigned)((a.n_q * a.n_heads + 3) / 4);
-  attn_combine_kernel<D><<<cgrid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 }  // namespace
@@ -569,15 +521,26 @@ int attn_mfma_rows_per_wg() { return BM; }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done, hipStream_t s) {
   const bool small = a.ps_log2 < 6;
-  if (kv_fp8) {
+  hipError_t e;
+  if (BCA_ATTN_WIDE && a.head_dim == 128 && !small) {
+    // 64 query rows per wave (same 256-row query tiles, flags and partials)
+    e = launch_attn_wide(a, kv_fp8, s);
+  } else if (BCA_ATTN_DMA && !kv_fp8 && a.head_dim == 128 && !small) {
+    // direct HBM -> LDS tile loads (same query tiles, flags and partials)
+    e = launch_attn_dma(a, s);
+  } else if (kv_fp8) {
     if (a.head_dim != 128 || small) return hipErrorInvalidValue;
-    return launch_t<128, true, false>(a, main_done, s);
+    e = launch_t<128, true, false>(a, s);
+  } else {
+    switch (a.head_dim) {
+      case 64: e = small ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s); break;
+      case 128: e = small ? launch_t<128, false, true>(a, s) : launch_t<128, false, false>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
   }
-  switch (a.head_dim) {
-    case 64: return small ? launch_t<64, false, true>(a, main_done, s) : launch_t<64, false, false>(a, main_done, s);
-    case 128: return small ? launch_t<128, false, true>(a, main_done, s) : launch_t<128, false, false>(a, main_done, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (e == hipSuccess && main_done) e = hipEventRecord(main_done, s);
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_attn_combine(a, s);
 }
 
 }  // namespace bca
