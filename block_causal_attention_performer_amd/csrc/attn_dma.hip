@@ -1,6 +1,6 @@
 // Block-causal attention over the paged KV cache: bf16 MFMA kernel whose
 // K / V^T tiles move HBM -> LDS by direct 16-byte LDS loads (gfx950
-// global_load_lds_dwordx4), head dim 128, pages of >= 64 keys.
+// buffer_load_dwordx4 ... lds), head dim 128, pages of >= 64 keys.
 //
 // Visibility (explainer "wan-streamer-realtime-av", listening-while-speaking
 // section and its figure caption; youleyou.com article section 3.1): query
@@ -22,6 +22,13 @@
 // group waits for its own previous tile (vmcnt) before the barrier that
 // publishes it.  V values of keys past n_kv are zeroed in LDS after they
 // land (tail tile only).
+//
+// The loads use the buffer (MUBUF) form with a per-tile descriptor, not the
+// global (FLAT-encoded) form: the compiler treats a FLAT direct load in
+// flight as a possible LDS access of unknown order and then drains every
+// LDS read before each use (lgkmcnt(0) every few MFMAs of the matrix
+// phase), while a buffer load counts on vmcnt only and the matrix phase
+// keeps three reads in flight.
 #include <math.h>
 
 #include <type_traits>
@@ -46,7 +53,6 @@ template <int N>
 using ic = std::integral_constant<int, N>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef const __attribute__((address_space(1))) void* gbl_ptr;
 
 // s_waitcnt with only vmcnt = n (lgkmcnt and expcnt left alone)
 template <int N>
@@ -159,9 +165,13 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     const char* base = group_b ? vpages + (((ph * D) << ps_log2) + (k0 & psm)) * 2
                                : kpages + ((((ph << ps_log2) | (k0 & psm)) * D) * 2);
     char* l = dst + gw * 1024;
+    // raw descriptor over the tile: stride 0, no range limit, gfx9 default
+    // data format; lane offsets stay below 2^31 for pages up to 2^20 keys
+    // (the dispatcher's bound for this kernel)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000);
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_ptr)(base + i * gstep + goff), (lds_ptr)(l + i * 4096), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(l + i * 4096), 16, (int)(i * gstep + goff), 0, 0, 0);
   };
   // group B, tail tile: zero the V^T entries of keys >= n_kv once they
   // landed.  Chunk position c of head-dim row d holds the keys

@@ -525,7 +525,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done
   if (BCA_ATTN_WIDE && a.head_dim == 128 && !small) {
     // 64 query rows per wave (same 256-row query tiles, flags and partials)
     e = launch_attn_wide(a, kv_fp8, s);
-  } else if (BCA_ATTN_DMA && !kv_fp8 && a.head_dim == 128 && !small) {
+  } else if (BCA_ATTN_DMA && !kv_fp8 && a.head_dim == 128 && !small && a.ps_log2 <= 20) {
     // direct HBM -> LDS tile loads (same query tiles, flags and partials)
     e = launch_attn_dma(a, s);
   } else if (kv_fp8) {
