@@ -235,6 +235,12 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       char* vprev = vslot(ic<rp>{});
       // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T
       f32x16 s[2];
+      // The two waves sharing a SIMD (one per group) are always in opposite
+      // phases.  The issue arbiter favours older waves, so without this
+      // group B's MFMAs and LDS reads queue behind group A's softmax; with
+      // it, whichever wave is in its matrix phase issues first and the
+      // softmax fills the gaps.
+      __builtin_amdgcn_s_setprio(2);
       {
         // opaque per-iteration copies: keep the read addresses from being
         // precomputed for all three slots outside the loop
@@ -269,6 +275,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       lds_barrier();
 
       // ---------------- vector phase: next tile two ahead into the free

@@ -275,6 +275,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
       // that order (the compiler would otherwise regroup the MFMAs and wait
       // for every outstanding read).
       f32x16 s[2];
+      // priority to the wave in its matrix phase (the issue arbiter favours
+      // older waves, which would put group B's MFMAs behind group A's softmax)
+      __builtin_amdgcn_s_setprio(2);
       {
         uint32_t xk = kx ^ (uint32_t)(kslot * (BN * D * 2));
         uint32_t xv = vx ^ (uint32_t)(vprev * (D * BN * 2));
@@ -308,6 +311,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       const float ks = FP8 ? kscale[kslot] : 1.0f;
       const float vs = FP8 ? vscale[vslot] : 1.0f;
       lds_barrier();
