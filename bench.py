@@ -31,7 +31,10 @@ METRIC = "block-causal attn TFLOP/s (% MFMA peak) + ms/160ms-unit at v0.2 shapes
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 UNIT_BUDGET_MS = 160.0
-ATTN_KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_performer_amd", "csrc", "attn_mfma.hip")
+# sources of the bf16 attention kernel the bench times (direct-load kernel)
+ATTN_KERNEL_SRCS = [os.path.join(ROOT, "block_causal_attention_performer_amd", "csrc", f)
+                    for f in ("attn_dma.hip", "attn_common.h")]
+ATTN_KERNEL_NAME = "attn_dma_kernel<128>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_v02_unit_traffic.txt")
 
 
@@ -63,7 +66,10 @@ class Hip:
 
 
 def _kernel_hash() -> str:
-    return hashlib.sha256(open(ATTN_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ATTN_KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(flops_unit_bytes=None):
@@ -237,7 +243,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(), "kernel": "attn_fwd_kernel<128>",
+                     "traffic": _traffic(), "kernel": ATTN_KERNEL_NAME,
                      "avg_launch_ms": round(attn_avg, 4), "flops_per_launch": flops_call},
         "kernels": {
             "kv_append": {"median_ms": round(app_med, 5), "bytes": app_bytes,
