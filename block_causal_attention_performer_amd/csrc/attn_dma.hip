@@ -113,6 +113,10 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
 
   const int64_t qrow = r0 + wave * QW + col;
   const int64_t lim = min(a.n_kv, ((a.q_pos0 + qrow) / B + 1) * B);
+  // a wave whose rows all lie past n_q (the ragged last query tile) keeps
+  // staging its share of the tiles and meeting the barriers but computes
+  // nothing: its SIMD partner then runs its phases uncontended
+  const bool idle = r0 + wave * QW >= a.n_q;
 
   bf16x8 qf[KK];
   {
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       // it, whichever wave is in its matrix phase issues first and the
       // softmax fills the gaps.
       __builtin_amdgcn_s_setprio(2);
-      {
+      if (!idle) {
         // opaque per-iteration copies: keep the read addresses from being
         // precomputed for all three slots outside the loop
         uint32_t xk = kx, xv = vx, kro = krow, vro = vrow;
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       const int tn = min(t + 2, tl);
       if (!group_b) stage(tn, kslot(ic<rp>{}));
       else stage(tn, vslot(ic<rp>{}));
-      {
+      if (!idle) {
         const int64_t k0 = (int64_t)t * BN;
         if (k0 + BN > lim_first) {
           const int lrel = (int)min(lim - k0, (int64_t)BN);
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     if (t <= tl) iter(t, ic<0>{});
     if (t + 1 <= tl) iter(t + 1, ic<1>{});
     // O += V(last)^T P(last)^T: V(tl) sits in slot (tl - t0) % 3
-    {
+    if (!idle) {
       const int rl = (tl - t0) % 3;
       const char* vl = rl == 0 ? lv0 : (rl == 1 ? lv1 : lv2);
       const char* vbase = vl + vrow;
