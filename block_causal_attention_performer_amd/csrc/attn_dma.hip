@@ -29,8 +29,16 @@
 // LDS read before each use (lgkmcnt(0) every few MFMAs of the matrix
 // phase), while a buffer load counts on vmcnt only and the matrix phase
 // keeps three reads in flight.
+//
+// Scheduling: one persistent workgroup per CU takes (query tile, split,
+// head) items from per-XCD work queues in the workspace (its own XCD's
+// first, then the others), and the key-range splits are cut 2 : ... : 2 : 1
+// so short items come last.  With one workgroup per item the launch ended
+// when the slowest XCD's share did (XCDs differ by several percent in
+// speed under this load) and the last round of items left CUs idle.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -91,25 +99,57 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   const bool group_b = wave >= NW / 2;
   const int gw = wave & 3;                   // wave index inside its group
 
-  // XCD-aware mapping (consecutive block ids go to the 8 XCDs in turn).
-  const int G = gridDim.x;
-  const int lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int H = a.n_heads;
   const int nqt = (int)((a.n_q + BM - 1) / BM);
-  if (lid >= nqt * H * a.nsplit) return;
-  const int qt = lid % nqt;
-  const int rest = lid / nqt;
-  const int split = rest % a.nsplit;
-  const int h = rest / a.nsplit;
 
+  // ------------------------------------------------------------ work queues
+  // One queue per XCD holds the items of its share of the heads, every first
+  // split before every second split and so on (query tiles of one head and
+  // split next to each other, so they stream the same K/V through that
+  // XCD's L2 together).  A persistent workgroup takes items from the queue
+  // of the XCD it runs on and, once that is empty, from the others: the
+  // launch ends when the last item does, whatever speed each XCD runs at.
+  // Thread 0 (group A) claims the next item as soon as its own part of the
+  // current one is done, while group B still runs its last phase; claiming
+  // any earlier would hold items back from CUs that fall idle at the end.
+  auto heads_lo = [&](int x) { return (x * H + kAttnQueues - 1) / kAttnQueues; };
+  auto qlen = [&](int x) { return (heads_lo(x + 1) - heads_lo(x)) * nqt * a.nsplit; };
+  __shared__ int item_sh[2];
+  int cur_q = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (31 << 11)) & (kAttnQueues - 1));
+  uint32_t dead = 0;                         // thread 0: queues found empty
+  // item from claim pv of queue cur_q, else from the other queues; -1 when all are empty
+  auto settle = [&](int pv) -> int {
+    if (pv < qlen(cur_q)) return (cur_q << 24) | pv;
+    dead |= 1u << cur_q;
+    for (int k = 1; k < kAttnQueues; ++k) {
+      const int x = (cur_q + k) & (kAttnQueues - 1);
+      if ((dead >> x) & 1) continue;
+      const int n = qlen(x);
+      const int v = n > 0 ? atomicAdd(a.sched + x, 1) : 0;
+      if (v < n) {
+        cur_q = x;
+        return (x << 24) | v;
+      }
+      dead |= 1u << x;
+    }
+    return -1;
+  };
+
+  // one (query tile, key-range split, head) item; thread 0 leaves the next
+  // item in item_sh[nxt]
+  auto work = [&](const int qt, const int split, const int h, const int nxt) {
   const int64_t B = a.block_size;
   const int64_t r0 = (int64_t)qt * BM;
   const int64_t rlast = (r0 + BM < a.n_q ? r0 + BM : a.n_q) - 1;
   const int64_t lim_first = min(a.n_kv, ((a.q_pos0 + r0) / B + 1) * B);
   const int64_t lim_last = min(a.n_kv, ((a.q_pos0 + rlast) / B + 1) * B);
   const int ntile = (int)((lim_last + BN - 1) / BN);
-  const int t_begin = (int)((int64_t)split * ntile / a.nsplit);
-  const int t_end = (int)((int64_t)(split + 1) * ntile / a.nsplit);
+  // splits in the ratio 2 : 2 : ... : 2 : 1: the last split's items are
+  // half as long and fill the end of the launch (2 : 1 measured best
+  // among 1 : 1, 3 : 2, 2 : 1, 5 : 2, 3 : 1, 4 : 1 and 8 : 1)
+  const int wsum = 2 * (a.nsplit - 1) + 1;
+  const int t_begin = (int)((int64_t)ntile * (2 * split) / wsum);
+  const int t_end = split + 1 == a.nsplit ? ntile : (int)((int64_t)ntile * (2 * split + 2) / wsum);
 
   const int64_t qrow = r0 + wave * QW + col;
   const int64_t lim = min(a.n_kv, ((a.q_pos0 + qrow) / B + 1) * B);
@@ -357,8 +397,11 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pp[c], o[db], 0, 0, 0);
       }
     }
+    if (tid == 0) item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
     if (!group_b) lds_barrier();           // balance group B's extra barrier
-    wait_vm<0>();                          // no direct load outlives the workgroup
+    wait_vm<0>();                          // no direct load outlives the item
+  } else if (tid == 0) {
+    item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
   }
 
   // one flag per (query tile, split, wave), written unconditionally
@@ -423,13 +466,42 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       ml[1] = l_tot;
     }
   }
+  };
+
+  // LDS-only barriers between items: the partial stores of an item need
+  // not land before the next one starts
+  if (tid == 0) item_sh[0] = settle(qlen(cur_q) > 0 ? atomicAdd(a.sched + cur_q, 1) : 0);
+  lds_barrier();
+  for (int k = 0;; k ^= 1) {
+    const int item = item_sh[k];
+    if (item < 0) break;
+    const int x = item >> 24, v = item & 0xFFFFFF;
+    const int hl = heads_lo(x);
+    const int per = (heads_lo(x + 1) - hl) * nqt;
+    const int split = v / per;
+    const int rem = v - split * per;
+    work(rem % nqt, split, hl + rem / nqt, k ^ 1);
+    lds_barrier();                           // next item visible; LDS rings free
+  }
+}
+
+__global__ void attn_sched_reset_kernel(int32_t* sched) {
+  if (threadIdx.x < kAttnQueues) sched[threadIdx.x] = 0;
 }
 
 hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t s) {
-  if (a.head_dim != 128 || a.ps_log2 < 6) return hipErrorInvalidValue;
+  if (a.head_dim != 128 || a.ps_log2 < 6 || !a.sched) return hipErrorInvalidValue;
+  if ((int64_t)a.n_heads * ((a.n_q + BM - 1) / BM) * a.nsplit >= (int64_t{1} << 24))
+    return hipErrorInvalidValue;             // item numbers must fit 24 bits
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
   const int64_t nqt = (a.n_q + BM - 1) / BM;
   const int64_t total = nqt * a.n_heads * a.nsplit;
-  const unsigned grid = (unsigned)((total + 7) / 8 * 8);
+  // one persistent workgroup per CU (the LDS rings allow one per CU)
+  const unsigned grid = (unsigned)std::min<int64_t>(total, std::max(ncu, 1));
+  attn_sched_reset_kernel<<<1, 64, 0, s>>>(a.sched);
   attn_dma_kernel<128><<<grid, NT, 0, s>>>(a);
   return hipGetLastError();
 }

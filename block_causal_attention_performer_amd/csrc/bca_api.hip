@@ -92,7 +92,8 @@ struct AttnPlan {
   size_t o_bytes;
 };
 
-// Attention workspace: overflow flags, then (with a split) the partials.
+// Attention workspace: overflow flags, the work-queue counters, then (with a
+// split) the partials.
 size_t attn_flag_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
   const int64_t BM = attn_mfma_rows_per_wg();
   const int64_t nqt = (n_q + BM - 1) / BM;
@@ -101,7 +102,7 @@ size_t attn_flag_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
 size_t attn_split_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
   const size_t per = (size_t)nsplit * n_q * c->n_heads;
   const size_t parts = nsplit > 1 ? align256(per * c->head_dim * 4) + align256(per * 2 * 4) : 0;
-  return attn_flag_bytes(c, n_q, nsplit) + parts;
+  return attn_flag_bytes(c, n_q, nsplit) + kAttnSchedBytes + parts;
 }
 
 // Workspace layout: [W transposed to bf16 hi/lo, 64 bytes per row of W]
@@ -191,6 +192,8 @@ bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t bloc
     char* ws = static_cast<char*>(workspace);
     a.flags_out = reinterpret_cast<int32_t*>(ws);
     ws += attn_flag_bytes(c, n_q, a.nsplit);
+    a.sched = reinterpret_cast<int32_t*>(ws);
+    ws += kAttnSchedBytes;
     if (a.nsplit > 1) {
       const size_t per = (size_t)a.nsplit * n_q * c->n_heads;
       a.ws_o = reinterpret_cast<float*>(ws);

@@ -16,6 +16,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeyTile = 64;        // keys per attention tile (a tile never straddles a >=64 page)
 constexpr int kAttnFlagWaves = 8;   // overflow flags per (query tile, split) of the fast attention kernel
+constexpr int kAttnQueues = 8;      // work queues of the persistent bf16 attention kernel, one per XCD
+constexpr size_t kAttnSchedBytes = 256;   // workspace bytes for their counters
 
 // ---------------------------------------------------------------- launchers
 
@@ -47,6 +49,7 @@ struct AttnArgs {
   float* ws_o;       // split partials: [nsplit][n_q][H][D] fp32 (unnormalised)
   float* ws_ml;      // [nsplit][n_q][H][2]  (reference max in log2 units, row sum)
   int32_t* flags_out;    // fast kernel: [H][n_qtiles][nsplit][kAttnFlagWaves] overflow flags
+  int32_t* sched;        // fast kernel: kAttnQueues work-queue counters (zeroed by its launch)
   const int32_t* flags;  // exact kernel: recompute only query tiles flagged here
   int32_t flag_splits;   // nsplit the flags were written with
   int64_t n_q;
