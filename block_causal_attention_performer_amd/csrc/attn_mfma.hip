@@ -462,34 +462,51 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-// Merge the nsplit partials of every (row, head) in split order:
+// Merge the NS partials of every (row, head) in split order:
 // M = max m_s, O = sum 2^(m_s - M) O_s / sum 2^(m_s - M) l_s.
-template <int D>
+// 32 lanes per (row, head), D / 32 consecutive values each; the split count
+// is a template argument, so every split's (m, l) and partial row are
+// loaded at once.
+template <int D, int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (row, head)
-  const int lane = threadIdx.x & 63;
+  constexpr int PER = D / 32;
+  static_assert(PER == 2 || PER == 4, "head dim 64 or 128");
+  using vec = float __attribute__((ext_vector_type(PER)));
+  const int64_t item = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);   // (row, head)
+  const int lane = threadIdx.x & 31;
   const int H = a.n_heads;
   if (item >= a.n_q * H) return;
   const int64_t stride = a.n_q * H;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_ml[(s * stride + item) * 2]);
-  constexpr int PER = D / 64;
-  float acc[PER > 0 ? PER : 1] = {};
-  float L = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float ms = a.ws_ml[(s * stride + item) * 2];
-    const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-    L += w * a.ws_ml[(s * stride + item) * 2 + 1];
-    const float* op = a.ws_o + (s * stride + item) * D;
+  float2 ml[NS];
+  vec os[NS];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * op[lane * PER + e];
+  for (int s = 0; s < NS; ++s) {
+    ml[s] = *reinterpret_cast<const float2*>(a.ws_ml + (s * stride + item) * 2);
+    os[s] = *reinterpret_cast<const vec*>(a.ws_o + (s * stride + item) * D + lane * PER);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, ml[s].x);
+  vec acc = {};
+  float L = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float w = ml[s].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[s].x - M);
+    L += w * ml[s].y;
+    acc += w * os[s];
   }
   const float inv = 1.0f / L;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int64_t off = item * D + lane * PER + e;
-    if (a.out_f32) static_cast<float*>(a.out)[off] = acc[e] * inv;
-    else reinterpret_cast<__bf16*>(a.out)[off] = (__bf16)(acc[e] * inv);
+  const int64_t off = item * D + lane * PER;
+  if (a.out_f32) {
+    *reinterpret_cast<vec*>(static_cast<float*>(a.out) + off) = acc * inv;
+  } else if constexpr (PER == 4) {
+    uint2 u;
+    u.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)});
+    u.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(acc[2] * inv), (__bf16)(acc[3] * inv)});
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) = u;
+  } else {
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + off) =
+        __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)});
   }
 }
 
@@ -500,14 +517,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #define BCA_ATTN_DMA 1
 #endif
 
+namespace {
+template <int D, int NS>
+hipError_t combine_ns(const AttnArgs& a, hipStream_t s) {
+  if constexpr (NS > kMaxAttnSplit) {
+    return hipErrorInvalidValue;
+  } else {
+    if (a.nsplit != NS) return combine_ns<D, NS + 1>(a, s);
+    const unsigned cgrid = (unsigned)((a.n_q * a.n_heads + 7) / 8);
+    attn_combine_kernel<D, NS><<<cgrid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+}
+}  // namespace
+
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
-  const unsigned cgrid = (unsigned)((a.n_q * a.n_heads + 3) / 4);
+  if (a.nsplit < 2 || a.nsplit > kMaxAttnSplit) return hipErrorInvalidValue;
   switch (a.head_dim) {
-    case 64: attn_combine_kernel<64><<<cgrid, 256, 0, s>>>(a); break;
-    case 128: attn_combine_kernel<128><<<cgrid, 256, 0, s>>>(a); break;
+    case 64: return combine_ns<64, 2>(a, s);
+    case 128: return combine_ns<128, 2>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 namespace {

@@ -12,8 +12,6 @@ using namespace bca;
 
 namespace {
 
-constexpr int kMaxAttnSplit = 8;
-
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int64_t x) { int l = 0; while ((int64_t{1} << l) < x) ++l; return l; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeyTile = 64;        // keys per attention tile (a tile never straddles a >=64 page)
 constexpr int kAttnFlagWaves = 8;   // overflow flags per (query tile, split) of the fast attention kernel
+constexpr int kMaxAttnSplit = 8;    // most key-range splits of one attention call
 constexpr int kAttnQueues = 8;      // work queues of the persistent bf16 attention kernel, one per XCD
 constexpr size_t kAttnSchedBytes = 256;   // workspace bytes for their counters
 
