@@ -103,9 +103,9 @@ size_t attn_split_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
   return attn_flag_bytes(c, n_q, nsplit) + kAttnSchedBytes + parts;
 }
 
-// Workspace layout: [W transposed to bf16 hi/lo, 64 bytes per row of W]
-// [attention: overflow flags, split partials].
-size_t euler_wt_bytes(int64_t k) { return align256((size_t)k * 16 * 2 * 2); }
+// Workspace layout: [velocity-projection partials, kEulerChunks x 64 bytes
+// per token] [attention: overflow flags, queue counters, split partials].
+size_t euler_ws_bytes(int64_t n_tok) { return align256((size_t)kEulerChunks * n_tok * 16 * 4); }
 
 // Pick the number of key-range splits: enough workgroups to fill every CU
 // for the last wave without making the partial round trips dominate.
@@ -229,14 +229,12 @@ bca_status check_euler(float* z, const void* x, const float* w, int64_t n_tok, i
 }
 
 bool euler_mfma_ok(const float* w, int32_t k, int32_t n_ch, int32_t x_dtype) {
-  return w && x_dtype == BCA_BF16 && n_ch == 16 && k % 32 == 0;
+  return w && x_dtype == BCA_BF16 && n_ch == 16 && k % (32 * kEulerChunks) == 0 && k <= kEulerMaxK;
 }
 
-// wt: transposed W halves already in the workspace (performer_unit prepares
-// them once per unit), or nullptr to prepare them here when there is room.
 bca_status enqueue_euler(float* z, const void* x, const float* w, int64_t n_tok, int32_t k,
                          int32_t n_ch, float dtau, int32_t x_dtype, void* workspace,
-                         size_t workspace_bytes, bool wt_ready, hipStream_t s) {
+                         size_t workspace_bytes, hipStream_t s) {
   if (n_tok == 0) return BCA_OK;
   EulerArgs a{};
   a.z = z;
@@ -249,12 +247,10 @@ bca_status enqueue_euler(float* z, const void* x, const float* w, int64_t n_tok,
   hipError_t e;
   if (!w) {
     e = launch_euler_plain(a, s);
-  } else if (euler_mfma_ok(w, k, n_ch, x_dtype) && workspace && workspace_bytes >= euler_wt_bytes(k)) {
-    a.wt_hi = static_cast<const uint16_t*>(workspace);
-    a.wt_lo = a.wt_hi + (size_t)k * 16;
-    e = wt_ready ? hipSuccess
-                 : launch_w_prep(w, const_cast<uint16_t*>(a.wt_hi), const_cast<uint16_t*>(a.wt_lo), k, s);
-    if (e == hipSuccess) e = launch_euler_proj(a, s);
+  } else if (euler_mfma_ok(w, k, n_ch, x_dtype) && workspace &&
+             workspace_bytes >= euler_ws_bytes(n_tok)) {
+    a.part = static_cast<float*>(workspace);
+    e = launch_euler_proj(a, s);
   } else {
     e = launch_euler_generic(a, x_dtype == BCA_F32, s);
   }
@@ -279,7 +275,7 @@ const char* bca_status_string(int32_t st) {
 size_t bca_workspace_bytes(const bca_kv_cache* c, int64_t n_q, int64_t n_kv, int32_t n_ch) {
   if (!c || n_q <= 0 || n_kv <= 0 || c->n_heads <= 0 || c->head_dim <= 0) return 0;
   (void)n_ch;
-  return euler_wt_bytes((int64_t)c->n_heads * c->head_dim) + attn_split_bytes(c, n_q, kMaxAttnSplit);
+  return euler_ws_bytes(n_q) + attn_split_bytes(c, n_q, kMaxAttnSplit);
 }
 
 bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_new, int64_t n_new,
@@ -300,7 +296,7 @@ bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t
   char* ws = static_cast<char*>(workspace);
   size_t room = workspace_bytes;
   if (ws) {
-    const size_t skip = euler_wt_bytes((int64_t)c->n_heads * c->head_dim);
+    const size_t skip = euler_ws_bytes(n_q);
     if (room > skip) { ws += skip; room -= skip; } else { ws = nullptr; room = 0; }
   }
   return enqueue_attn(q, n_q, q_pos0, block_size, c, n_kv, out, out_dtype, softmax_scale, ws,
@@ -312,8 +308,7 @@ bca_status fm_euler_step(float* z, const void* x, const float* w, int64_t n_tok,
                          size_t workspace_bytes, hipStream_t s) {
   bca_status st = check_euler(z, x, w, n_tok, k, n_ch, dtau, x_dtype);
   if (st != BCA_OK) return st;
-  return enqueue_euler(z, x, w, n_tok, k, n_ch, dtau, x_dtype, workspace, workspace_bytes, false,
-                       s);
+  return enqueue_euler(z, x, w, n_tok, k, n_ch, dtau, x_dtype, workspace, workspace_bytes, s);
 }
 
 bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new, const void* q,
@@ -340,15 +335,10 @@ bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new,
   if (st != BCA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   size_t room = workspace ? workspace_bytes : 0;
-  const size_t wt_bytes = euler_wt_bytes(kdim);
-  const bool wt = euler_mfma_ok(w, kdim, n_ch, io) && room >= wt_bytes;
-  if (wt) {
-    // W's transposed halves, once per unit
-    uint16_t* hi = reinterpret_cast<uint16_t*>(ws);
-    if (launch_w_prep(w, hi, hi + (size_t)kdim * 16, kdim, s) != hipSuccess) return BCA_EHIP;
-  }
-  char* attn_ws = room > wt_bytes ? ws + wt_bytes : nullptr;
-  const size_t attn_room = room > wt_bytes ? room - wt_bytes : 0;
+  const size_t eu_bytes = euler_ws_bytes(n_q);
+  const bool eu = room >= eu_bytes;
+  char* attn_ws = room > eu_bytes ? ws + eu_bytes : nullptr;
+  const size_t attn_room = room > eu_bytes ? room - eu_bytes : 0;
   for (int32_t step = 0; step < n_steps; ++step) {
     hipEvent_t* ev = attn_events ? attn_events + 3 * step : nullptr;
     if (ev && hipEventRecord(ev[0], s) != hipSuccess) return BCA_EHIP;
@@ -356,8 +346,8 @@ bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new,
                       attn_room, ev ? ev[1] : nullptr, s);
     if (st != BCA_OK) return st;
     if (ev && hipEventRecord(ev[2], s) != hipSuccess) return BCA_EHIP;
-    st = enqueue_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io, wt ? ws : nullptr,
-                       wt ? wt_bytes : 0, wt, s);
+    st = enqueue_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io, eu ? ws : nullptr,
+                       eu ? eu_bytes : 0, s);
     if (st != BCA_OK) return st;
   }
   return BCA_OK;

@@ -17,6 +17,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kKeyTile = 64;        // keys per attention tile (a tile never straddles a >=64 page)
 constexpr int kAttnFlagWaves = 8;   // overflow flags per (query tile, split) of the fast attention kernel
 constexpr int kMaxAttnSplit = 8;    // most key-range splits of one attention call
+constexpr int kEulerChunks = 8;     // k-range parts of the velocity projection
+constexpr int kEulerMaxK = 8192;    // largest k the MFMA projection takes (32 k-steps per part)
 constexpr int kAttnQueues = 8;      // work queues of the persistent bf16 attention kernel, one per XCD
 constexpr size_t kAttnSchedBytes = 256;   // workspace bytes for their counters
 
@@ -89,15 +91,14 @@ struct EulerArgs {
   float* z;
   const void* x;
   const float* w;
-  const uint16_t* wt_hi;   // W transposed to [16][k], bf16 high half
-  const uint16_t* wt_lo;   // bf16 low half (W - hi)
+  float* part;             // projection partials [kEulerChunks][n_tok][16] (workspace)
   int64_t n_tok;
   int32_t k;
   int32_t n_ch;
   float dtau;
 };
-// W [k][16] fp32 -> wt_hi/wt_lo [16][k] bf16 (k * 64 bytes in total).
-hipError_t launch_w_prep(const float* w, uint16_t* wt_hi, uint16_t* wt_lo, int k, hipStream_t s);
+// v = x W (bf16 x, n_ch 16, k a multiple of 32 * kEulerChunks) and the
+// update, through the partials in a.part (two launches).
 hipError_t launch_euler_proj(const EulerArgs& a, hipStream_t s);
 hipError_t launch_euler_generic(const EulerArgs& a, bool x_f32, hipStream_t s);
 hipError_t launch_euler_plain(const EulerArgs& a, hipStream_t s);

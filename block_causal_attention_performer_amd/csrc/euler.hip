@@ -8,84 +8,124 @@
 //
 // bf16 x, n_ch = 16: the product runs on v_mfma_f32_16x16x32_bf16 with W
 // split into bf16 high and low halves (W = hi + lo to ~2^-16 relative), two
-// MFMAs per k-step, fp32 accumulation.  W is first rewritten transposed,
-// as hi/lo bf16 rows per channel (w_prep_kernel, 64 bytes per row of W, into
-// the caller's workspace), so every MFMA operand is one 16-byte load.  The
-// main kernel is bound by reading x from HBM once: one workgroup per 16
-// tokens, its sixteen waves split k (many loads in flight per CU, since a
-// unit has only a few hundred such token groups) and add their 16x16
-// partials through LDS in a fixed order before the update.
+// MFMAs per k-step, fp32 accumulation.  The launch is bound by reading x
+// from HBM once.  A workgroup takes 64 tokens and an eighth of k: it loads
+// its eighth of W (fp32, from L2), starts all its x loads, splits W into
+// hi/lo bf16 rows per channel in LDS while x streams in, then runs the MFMAs and sums its
+// eight waves' partials in a fixed order into the workspace; a second small
+// kernel adds the eight parts (fixed order) and updates z.  Splitting k
+// keeps each CU's share of W small: with every workgroup reading all of W,
+// W was twice the bytes of x per CU and the CUs' outstanding loads, not
+// HBM, set the pace; with 120 registers per lane two workgroups share a CU.
+#include <algorithm>
+
 #include "bca_internal.h"
 
 namespace bca {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kTok = 16;       // tokens per workgroup
-constexpr int kProjWaves = 16; // waves per projection workgroup (split k)
-constexpr int kBatch = 8;      // k-steps loaded ahead per wave
-
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
+constexpr int kRows = 64;      // tokens per projection workgroup (4 MFMA row tiles)
+constexpr int kPWaves = 8;     // waves per projection workgroup (split the k-steps)
+constexpr int kMaxSteps = 4;   // k-steps of 32 per wave kept in registers
 }  // namespace
 
-// W [k][16] fp32 -> wt_hi / wt_lo [16][k] bf16 with W = hi + lo (+ O(2^-16)).
-__global__ __launch_bounds__(kThreads) void w_prep_kernel(const float* w, uint16_t* wt_hi,
-                                                          uint16_t* wt_lo, int k) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= k * 16) return;
-  const int kk = i >> 4, c = i & 15;
-  const float f = w[i];
-  const uint16_t hi = bf16_rne(f);
-  wt_hi[(int64_t)c * k + kk] = hi;
-  wt_lo[(int64_t)c * k + kk] = bf16_rne(f - __uint_as_float((uint32_t)hi << 16));
-}
-
-__global__ __launch_bounds__(kProjWaves * 64) void euler_proj_kernel(EulerArgs a) {
-  __shared__ float part[kProjWaves][kTok * 16];
+__global__ __launch_bounds__(kPWaves * 64) void euler_proj_kernel(EulerArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = (int64_t)blockIdx.x * kTok + (lane & 15);
-  const bool rv = row < a.n_tok;
-  const int nsteps = a.k / 32;
-  const int s0 = wave * nsteps / kProjWaves, s1 = (wave + 1) * nsteps / kProjWaves;
-  const int oct = 8 * (lane >> 4);
-  const uint16_t* xp = static_cast<const uint16_t*>(a.x) + row * a.k + oct;
-  const uint16_t* hp = a.wt_hi + (int64_t)(lane & 15) * a.k + oct;
-  const uint16_t* lp = a.wt_lo + (int64_t)(lane & 15) * a.k + oct;
+  const int kch = a.k / kEulerChunks;        // k per workgroup
+  const int kc = blockIdx.y;
+  const int nst = kch / 32;                  // k-steps of the chunk
+  const int pitch = kch + 8;                 // bf16 per LDS row (16-byte pad: no bank conflicts)
+  uint16_t* whi = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* wlo = whi + 16 * pitch;
+  const int64_t r0 = (int64_t)blockIdx.x * kRows;
+  const int g = lane >> 4, ln = lane & 15;
 
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int sb = s0; sb < s1; sb += kBatch) {
-    u32x4 xr[kBatch], hr[kBatch], lr[kBatch];
+  // W's eighth first (from L2, it lands before the x stream), then every x
+  // fragment of this wave's k-steps (st = wave + kPWaves * j, all four row
+  // tiles); W is split and written to LDS while x is in flight.
+  // Unit u = 8 k-rows x 4 channels: hi = RNE(w), lo = RNE(w - hi).
+  const float* wb = a.w + (int64_t)kc * kch * 16;
+  const int nunit = (kch / 8) * 4;
+  static_assert(kEulerMaxK / kEulerChunks / 8 * 4 <= kPWaves * 64, "one W unit per thread");
+  f32x4 f[8];
+  if (tid < nunit) {
+    const int r8 = tid >> 2, q = tid & 3;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int st = sb + j;
-      const bool ok = st < s1;
-      xr[j] = (ok && rv) ? *reinterpret_cast<const u32x4*>(xp + 32 * st) : u32x4{0, 0, 0, 0};
-      hr[j] = ok ? *reinterpret_cast<const u32x4*>(hp + 32 * st) : u32x4{0, 0, 0, 0};
-      lr[j] = ok ? *reinterpret_cast<const u32x4*>(lp + 32 * st) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 8; ++i) f[i] = *reinterpret_cast<const f32x4*>(wb + (8 * r8 + i) * 16 + 4 * q);
+  }
+  u32x4 xr[kMaxSteps][4];
+  const uint16_t* xb = static_cast<const uint16_t*>(a.x) + (int64_t)kc * kch + 8 * g;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, hr[j]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, lr[j]), acc, 0, 0, 0);
+  for (int j = 0; j < kMaxSteps; ++j) {
+    const int st = wave + kPWaves * j;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int64_t row = r0 + 16 * rt + ln;
+      xr[j][rt] = (st < nst && row < a.n_tok)
+                      ? *reinterpret_cast<const u32x4*>(xb + row * a.k + 32 * st)
+                      : u32x4{0, 0, 0, 0};
     }
   }
-  // acc[e] = partial v[token 4*(lane>>4)+e][channel lane&15]
+  if (tid < nunit) {
+    const int r8 = tid >> 2, q = tid & 3;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) part[wave][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
+    for (int c = 0; c < 4; ++c) {
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)f[i][c];
+        hv[i] = h;
+        lv[i] = (__bf16)(f[i][c] - (float)h);
+      }
+      *reinterpret_cast<bf16x8*>(whi + (4 * q + c) * pitch + 8 * r8) = hv;
+      *reinterpret_cast<bf16x8*>(wlo + (4 * q + c) * pitch + 8 * r8) = lv;
+    }
+  }
   __syncthreads();
-  if (tid >= kTok * 16) return;
-  const int64_t tok = (int64_t)blockIdx.x * kTok + (tid >> 4);
-  if (tok < a.n_tok) {
+
+  f32x4 acc[4] = {};
+#pragma unroll
+  for (int j = 0; j < kMaxSteps; ++j) {
+    const int st = wave + kPWaves * j;
+    if (st < nst) {
+      const bf16x8 h = *reinterpret_cast<const bf16x8*>(whi + ln * pitch + 32 * st + 8 * g);
+      const bf16x8 l = *reinterpret_cast<const bf16x8*>(wlo + ln * pitch + 32 * st + 8 * g);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[j][rt]);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, h, acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, l, acc[rt], 0, 0, 0);
+      }
+    }
+  }
+  // acc[rt][e] = partial v[token 16 rt + 4 g + e][channel ln]; sum the
+  // waves in order through LDS (reusing the W rows)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(wave * kRows + 16 * rt + 4 * g + e) * 16 + ln] = acc[rt][e];
+  __syncthreads();
+  for (int i = tid; i < kRows * 16; i += kPWaves * 64) {
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kProjWaves; ++w) v += part[w][tid];
-    float* zp = a.z + tok * 16 + (tid & 15);
-    *zp = __builtin_fmaf(-a.dtau, v, *zp);
+    for (int w = 0; w < kPWaves; ++w) v += red[w * kRows * 16 + i];
+    const int64_t row = r0 + (i >> 4);
+    if (row < a.n_tok) a.part[((int64_t)kc * a.n_tok + row) * 16 + (i & 15)] = v;
   }
+}
+
+// z <- z - dtau * (sum of the k-part partials, in order)
+__global__ __launch_bounds__(kThreads) void euler_reduce_kernel(EulerArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= a.n_tok * 16) return;
+  float v = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kEulerChunks; ++c) v += a.part[c * a.n_tok * 16 + i];
+  a.z[i] = __builtin_fmaf(-a.dtau, v, a.z[i]);
 }
 
 // Any x dtype / n_ch <= 64 / k: one workgroup per token, fp32 FMA, fixed
@@ -130,15 +170,20 @@ __global__ __launch_bounds__(kThreads) void euler_plain_kernel(EulerArgs a) {
   a.z[i] = __builtin_fmaf(-a.dtau, static_cast<const float*>(a.x)[i], a.z[i]);
 }
 
-hipError_t launch_w_prep(const float* w, uint16_t* wt_hi, uint16_t* wt_lo, int k, hipStream_t s) {
-  const int n = k * 16;
-  w_prep_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(w, wt_hi, wt_lo, k);
-  return hipGetLastError();
-}
-
 hipError_t launch_euler_proj(const EulerArgs& a, hipStream_t s) {
-  if (a.n_ch != 16 || a.k % 32 != 0 || !a.wt_hi || !a.wt_lo) return hipErrorInvalidValue;
-  euler_proj_kernel<<<(unsigned)((a.n_tok + kTok - 1) / kTok), kProjWaves * 64, 0, s>>>(a);
+  const int kch = a.k / kEulerChunks;
+  static_assert(kEulerMaxK / kEulerChunks / 32 <= kPWaves * kMaxSteps, "k-steps per part");
+  if (a.n_ch != 16 || a.k % (32 * kEulerChunks) != 0 || a.k > kEulerMaxK || !a.part)
+    return hipErrorInvalidValue;
+  const size_t lds = std::max<size_t>((size_t)2 * 16 * (kch + 8) * 2, (size_t)kPWaves * kRows * 16 * 4);
+  const dim3 grid((unsigned)((a.n_tok + kRows - 1) / kRows), kEulerChunks);
+  hipError_t e = hipFuncSetAttribute((const void*)euler_proj_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  euler_proj_kernel<<<grid, kPWaves * 64, lds, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  euler_reduce_kernel<<<(unsigned)((a.n_tok * 16 + kThreads - 1) / kThreads), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
