@@ -118,6 +118,45 @@ def cpu_baseline(inp, w, rows_n, heads_n):
             "seconds": dt}
 
 
+def catchup(args, w, inp, cache, hip, stream, bca, workloads):
+    """Multi-block catch-up call: queries = the last N units of the cache
+    (history + the unit), block size = one unit, so future key tiles of every
+    query tile are skipped and only the diagonal block's tiles are masked.
+    Times the whole call (main kernel, split combine, exact rerun check)."""
+    bca.kv_append(cache, inp["k_new"], inp["v_new"])
+    q_pos0, n_q, flops = workloads.catchup_span(w, args.catchup_units)
+    H, D = w.n_heads, w.head_dim
+    q = workloads.qkv(workloads.seed_for(w.index, "q_catchup"), n_q, H, D, w.qkv_scale, "bf16", "cuda")
+    ws = bca.alloc_workspace(bca.workspace_bytes(cache, n_q, w.n_kv, w.n_ch))
+    out = torch.empty((n_q, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        bca.block_causal_attn(q, cache, n_kv=w.n_kv, q_pos0=q_pos0, block_size=w.unit_tokens,
+                              out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        call()
+    hip.record(e1, stream)
+    ms = hip.elapsed_ms(e0, e1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "multi-block catch-up attention TFLOP/s (% MFMA peak) at v0.2 shapes",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded device draws, 0.5*N(0,1) Q/K/V rounded to bf16)",
+        "config": {"workload": f"{w.name}_catchup{args.catchup_units}", "heads": H, "head_dim": D,
+                   "n_q": n_q, "q_pos0": q_pos0, "block_size": w.unit_tokens, "n_kv": w.n_kv,
+                   "page_size": w.page_size, "parallelism": "none"},
+        "flops_per_call": flops,
+        "call_pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +169,9 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (PMC calibration)")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--catchup-units", type=int, default=0,
+                    help="instead of the performer step, time one multi-block catch-up "
+                         "block_causal_attn call whose queries are the last N units of the cache")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -152,6 +194,9 @@ def main():
     pt = workloads.page_table(n_log, n_log + 1, 1234)
     cache = bca.KVCache(H, D, ps, pt, n_log + 1, w.dtype if w.dtype != "fp8" else "fp8", device=dev)
     bca.kv_append(cache, inp["k_hist"], inp["v_hist"])
+    if args.catchup_units > 0:
+        catchup(args, w, inp, cache, hip, stream, bca, workloads)
+        return
     ws = bca.alloc_workspace(bca.workspace_bytes(cache, lq, w.n_kv, w.n_ch))
     osc = torch.empty((lq, H, D), dtype=torch.bfloat16, device=dev)
     z = inp["eps"].clone()

@@ -101,3 +101,35 @@ def test_v02_performer_unit_sampled_rows():
     z_want = oracle.euler_solve(eps, lambda zz, tau: v, w.n_steps)
     assert_close(osc[ROWS.tolist()].float().cpu().numpy(), o_want, 2e-2, 1e-2, what="v0.2 unit O")
     assert_close(z[ROWS.tolist()].cpu().numpy(), z_want, 2e-2, 1e-2, what="v0.2 unit z")
+
+
+def test_v02_catchup_sampled_rows():
+    """Multi-block catch-up call at v0.2 shapes, in the configuration
+    `bench.py --workload v02_attn --catchup-units 8` times: the queries are
+    the last 8 units of the 122,496-key cache (29,696 rows, q_pos0 = 92,800,
+    blocks of 3712), so every query tile skips the key tiles of later blocks
+    and masks only its own block's.  Sampled rows at block edges (all heads)
+    against the oracle over each row's visible keys."""
+    say("v0.2 catch-up, 8 units of queries")
+    w, inp, g, _ = _setup("v02_attn")
+    bca.kv_append(g, inp["k_new"], inp["v_new"])
+    U, B = 8, w.unit_tokens
+    q_pos0, n_q, _ = workloads.catchup_span(w, U)
+    H, D = w.n_heads, w.head_dim
+    q = workloads.qkv(workloads.seed_for(w.index, "q_catchup"), n_q, H, D, w.qkv_scale, "bf16", "cuda")
+    ws = bca.alloc_workspace(bca.workspace_bytes(g, n_q, w.n_kv, w.n_ch))
+    out = bca.block_causal_attn(q, g, n_kv=w.n_kv, q_pos0=q_pos0, block_size=B, workspace=ws)
+    torch.cuda.synchronize()
+    rows = [0, 1, B - 1, B, 3 * B + 100, 5 * B - 1, 7 * B, n_q - 1]
+    k_all = torch.cat([inp["k_hist"], inp["k_new"]])
+    v_all = torch.cat([inp["v_hist"], inp["v_new"]])
+    qs = q[rows].float().cpu().numpy().astype(np.float64)
+    want = np.zeros((len(rows), H, D))
+    for h in range(H):
+        k = k_all[:, h].float().cpu().numpy().astype(np.float64)[:, None]
+        v = v_all[:, h].float().cpu().numpy().astype(np.float64)[:, None]
+        for i, r in enumerate(rows):
+            # the oracle's own block mask, for the row at global position q_pos0 + r
+            want[i, h] = oracle.attention_dense(qs[i:i + 1, None, h], k, v, q_pos0 + r, B)[0, 0]
+    got = out[rows].float().cpu().numpy()
+    assert_close(got, want, 2e-2, 1e-2, what="v0.2 catch-up sampled rows")

@@ -33,7 +33,7 @@ from typing import Optional
 import torch
 
 SLOTS = {"q": 0, "k_hist": 1, "v_hist": 2, "k_new": 3, "v_new": 4,
-         "eps": 5, "z0": 6, "w": 7}
+         "eps": 5, "z0": 6, "w": 7, "q_catchup": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -66,6 +66,19 @@ class Workload:
         """Algorithmic FLOPs of one streaming attention call: QK^T and PV over
         every visible (query, key) pair, 2*D each."""
         return 4.0 * self.n_heads * self.head_dim * self.unit_tokens * self.n_kv
+
+
+def catchup_span(w: Workload, units: int):
+    """Catch-up (multi-block) call on a workload's cache: the queries are
+    the last `units` units of the cache (q_pos0 = n_kv - units * B, block
+    size B = one unit), drawn from their own seed slot.  Returns (q_pos0,
+    n_q, algorithmic FLOPs): each block sees every earlier key and its own
+    block, so block b (0-based) costs 4*H*D*B*(q_pos0 + (b + 1) * B)."""
+    B = w.unit_tokens
+    n_q = units * B
+    q_pos0 = w.n_kv - n_q
+    keys = sum(q_pos0 + (b + 1) * B for b in range(units))
+    return q_pos0, n_q, 4.0 * w.n_heads * w.head_dim * B * keys
 
 
 WORKLOADS = {
