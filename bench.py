@@ -157,6 +157,58 @@ def catchup(args, w, inp, cache, hip, stream, bca, workloads):
         "call_pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}), flush=True)
 
 
+def stream_units(args, w, inp, bca, workloads):
+    """N consecutive performer units through a streaming session starting
+    from the workload's history: each unit's pages come from the free list
+    (every other v0.2 unit starts mid-page), eager and as replayed HIP graphs
+    (one warm-up unit each, then N timed units, wall clock)."""
+    H, D, ps, lq, S = w.n_heads, w.head_dim, w.page_size, w.unit_tokens, w.n_steps
+    N = args.stream_units
+    n_hist_pages = w.n_hist // ps
+    n_log = -(-(w.n_hist + (N + 1) * lq) // ps)
+    n_phys = n_log + 8
+    gen = torch.Generator().manual_seed(5)
+    units = []
+    for u in range(N + 1):
+        units.append([workloads.qkv(workloads.seed_for(w.index, slot) * 1000 + u + 1, lq, H, D,
+                                    w.qkv_scale, "bf16", "cuda") for slot in ("k_new", "v_new", "q")])
+    osc = torch.empty((lq, H, D), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for mode in ("eager", "graph"):
+        perm = torch.randperm(n_phys, generator=gen).to(torch.int32)
+        pt = torch.full((n_log,), -1, dtype=torch.int32)
+        pt[:n_hist_pages] = perm[:n_hist_pages]
+        cache = bca.KVCache(H, D, ps, pt, n_phys, "bf16")
+        bca.kv_append(cache, inp["k_hist"], inp["v_hist"])
+        ss = bca.Session(cache, perm[n_hist_pages:].tolist())
+        ws = bca.alloc_workspace(bca.workspace_bytes(cache, lq, w.n_hist + (N + 1) * lq, w.n_ch))
+        z = inp["eps"].clone()
+        k, v, q = units[0]
+        ss.unit(k, v, q, inp["w"], z, S, osc, workspace=ws, use_graph=mode == "graph")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for u in range(1, N + 1):
+            k, v, q = units[u]
+            z.copy_(inp["eps"])
+            ss.unit(k, v, q, inp["w"], z, S, osc, workspace=ws, use_graph=mode == "graph")
+        torch.cuda.synchronize()
+        res[mode] = (time.perf_counter() - t0) * 1e3 / N
+        assert cache.n_tokens == w.n_hist + (N + 1) * lq
+        ss.close()
+        del cache, ws
+    print(json.dumps({
+        "metric": "streaming performer units through a session, ms per unit at v0.2 shapes",
+        "value": round(res["graph"], 4), "unit": "ms/unit", "n_gpus": 1, "steps": N,
+        "warmup": 1, "ms_per_step": round(res["graph"], 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded device draws, 0.5*N(0,1) Q/K/V rounded to bf16)",
+        "config": {"workload": f"{w.name}_stream{N}", "heads": H, "head_dim": D, "unit_tokens": lq,
+                   "hist_tokens": w.n_hist, "page_size": ps, "solver_steps": S,
+                   "parallelism": "none"},
+        "eager_ms_per_unit": round(res["eager"], 4), "graph_ms_per_unit": round(res["graph"], 4),
+        "unit_budget_frac": round(res["graph"] / UNIT_BUDGET_MS, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +224,9 @@ def main():
     ap.add_argument("--catchup-units", type=int, default=0,
                     help="instead of the performer step, time one multi-block catch-up "
                          "block_causal_attn call whose queries are the last N units of the cache")
+    ap.add_argument("--stream-units", type=int, default=0,
+                    help="instead of the performer step, stream N consecutive units through a "
+                         "session (page allocation, mid-page appends), eager and as HIP graphs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -196,6 +251,10 @@ def main():
     bca.kv_append(cache, inp["k_hist"], inp["v_hist"])
     if args.catchup_units > 0:
         catchup(args, w, inp, cache, hip, stream, bca, workloads)
+        return
+    if args.stream_units > 0:
+        del cache
+        stream_units(args, w, inp, bca, workloads)
         return
     ws = bca.alloc_workspace(bca.workspace_bytes(cache, lq, w.n_kv, w.n_ch))
     osc = torch.empty((lq, H, D), dtype=torch.bfloat16, device=dev)

@@ -78,12 +78,21 @@ def lib() -> ctypes.CDLL:
     L.bca_workspace_bytes.restype = sz
     L.bca_status_string.argtypes = [i32]
     L.bca_status_string.restype = ctypes.c_char_p
+    L.bca_session_create.argtypes = [cp, ctypes.POINTER(i32), i32, ctypes.POINTER(vp)]
+    L.bca_session_create.restype = i32
+    L.bca_session_unit.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, sz, i32, vp]
+    L.bca_session_unit.restype = i32
+    L.bca_session_free_pages.argtypes = [vp]
+    L.bca_session_free_pages.restype = i64
+    L.bca_session_destroy.argtypes = [vp]
+    L.bca_session_destroy.restype = None
     _lib = L
     return L
 
 
 EXPORTS = ("kv_append", "block_causal_attn", "fm_euler_step", "performer_unit",
-           "bca_workspace_bytes", "bca_status_string")
+           "bca_workspace_bytes", "bca_status_string", "bca_session_create", "bca_session_unit",
+           "bca_session_free_pages", "bca_session_destroy")
 
 
 def status_string(status: int) -> str:
@@ -224,3 +233,44 @@ def performer_unit(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: 
         ev, _stream(stream))
     _check(st, "performer_unit")
     return z
+
+
+class Session:
+    """Streaming session over one growing cache (bca_session_*): each unit()
+    maps the logical pages the unit reaches onto the next free physical
+    pages, then runs one performer unit, optionally as a replayed HIP graph."""
+
+    def __init__(self, cache: KVCache, free_pages: Sequence[int]):
+        self.cache = cache
+        arr = (ctypes.c_int32 * len(free_pages))(*[int(p) for p in free_pages])
+        h = ctypes.c_void_p()
+        _check(lib().bca_session_create(ctypes.byref(cache.c), arr, len(free_pages), ctypes.byref(h)),
+               "bca_session_create")
+        self.h = h
+
+    def unit(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, w: torch.Tensor,
+             z: torch.Tensor, n_steps: int, o_scratch: torch.Tensor,
+             workspace: Optional[torch.Tensor] = None, use_graph: bool = False,
+             stream=None) -> torch.Tensor:
+        st = lib().bca_session_unit(
+            self.h, _ptr(k_new), _ptr(v_new), _ptr(q), q.shape[0], _ptr(w), _ptr(z), z.shape[1],
+            n_steps, _ptr(o_scratch), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            1 if use_graph else 0, _stream(stream))
+        _check(st, "bca_session_unit")
+        return z
+
+    @property
+    def free_pages(self) -> int:
+        return int(lib().bca_session_free_pages(self.h))
+
+    def close(self) -> None:
+        if self.h is not None and self.h.value:
+            lib().bca_session_destroy(self.h)
+        self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

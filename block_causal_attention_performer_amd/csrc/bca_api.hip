@@ -5,6 +5,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <new>
+#include <vector>
 
 #include "bca_internal.h"
 
@@ -257,7 +259,80 @@ bca_status enqueue_euler(float* z, const void* x, const float* w, int64_t n_tok,
   return e == hipSuccess ? BCA_OK : BCA_EHIP;
 }
 
+// performer_unit in two passes, so a caller that must change state between
+// validation and launch (the streaming session) can validate first.
+bca_status check_performer(const bca_kv_cache* c, const void* k_new, const void* v_new,
+                           const void* q, int64_t n_q, const float* w, float* z, int32_t n_ch,
+                           int32_t n_steps, void* o_scratch) {
+  if (!c || !q || !w || !z || !o_scratch || n_q <= 0 || n_steps <= 0) return BCA_EINVAL;
+  const int32_t io = c->dtype == BCA_F32 ? BCA_F32 : BCA_BF16;
+  bca_status st = check_append(c, k_new, v_new, n_q, io);
+  if (st != BCA_OK) return st;
+  const int64_t n_kv = c->n_tokens + n_q;
+  bca_kv_cache after = *c;
+  after.n_tokens = n_kv;
+  st = check_attn(q, n_q, n_kv - n_q, (int32_t)n_q, &after, n_kv, o_scratch, io, io, 0.0f);
+  if (st != BCA_OK) return st;
+  const int32_t kdim = c->n_heads * c->head_dim;
+  st = check_euler(z, o_scratch, w, n_q, kdim, n_ch, 1.0f / (float)n_steps, io);
+  if (st != BCA_OK) return st;
+  if (n_q > INT32_MAX) return BCA_EINVAL;
+  return BCA_OK;
+}
+
+bca_status enqueue_performer(bca_kv_cache* c, const void* k_new, const void* v_new, const void* q,
+                             int64_t n_q, const float* w, float* z, int32_t n_ch, int32_t n_steps,
+                             void* o_scratch, void* workspace, size_t workspace_bytes,
+                             hipEvent_t* attn_events, hipStream_t s) {
+  const int32_t io = c->dtype == BCA_F32 ? BCA_F32 : BCA_BF16;
+  const int64_t n_kv = c->n_tokens + n_q;
+  const int32_t kdim = c->n_heads * c->head_dim;
+  const float dtau = 1.0f / (float)n_steps;
+  bca_status st = enqueue_append(c, k_new, v_new, n_q, s);
+  if (st != BCA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  size_t room = workspace ? workspace_bytes : 0;
+  const size_t eu_bytes = euler_ws_bytes(n_q);
+  const bool eu = room >= eu_bytes;
+  char* attn_ws = room > eu_bytes ? ws + eu_bytes : nullptr;
+  const size_t attn_room = room > eu_bytes ? room - eu_bytes : 0;
+  for (int32_t step = 0; step < n_steps; ++step) {
+    hipEvent_t* ev = attn_events ? attn_events + 3 * step : nullptr;
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return BCA_EHIP;
+    st = enqueue_attn(q, n_q, n_kv - n_q, (int32_t)n_q, c, n_kv, o_scratch, io, 0.0f, attn_ws,
+                      attn_room, ev ? ev[1] : nullptr, s);
+    if (st != BCA_OK) return st;
+    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return BCA_EHIP;
+    st = enqueue_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io, eu ? ws : nullptr,
+                       eu ? eu_bytes : 0, s);
+    if (st != BCA_OK) return st;
+  }
+  return BCA_OK;
+}
+
+// Streaming session: page-table entries for newly mapped logical pages are
+// written by a kernel on the stream (values in the kernel arguments, so a
+// captured graph carries them), before the unit's append reads them.
+constexpr int kPtBatch = 32;
+struct PtUpdate {
+  int32_t lp0, count;
+  int32_t phys[kPtBatch];
+};
+__global__ void pt_set_kernel(int32_t* pt, PtUpdate u) {
+  const int i = (int)threadIdx.x;
+  if (i < u.count) pt[u.lp0 + i] = u.phys[i];
+}
+
 }  // namespace
+
+struct bca_session {
+  bca_kv_cache* cache;
+  std::vector<int32_t> free_pages;   // handed out in this order
+  size_t next_free;
+  int64_t mapped;                    // logical pages [0, mapped) have physical pages
+  hipGraphExec_t exec;               // last instantiated unit graph (updated in place)
+  hipStream_t cap;                   // capture-only stream (nothing executes on it)
+};
 
 extern "C" {
 
@@ -316,41 +391,116 @@ bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new,
                           void* o_scratch, void* workspace, size_t workspace_bytes,
                           hipEvent_t* attn_events, hipStream_t s) {
   // validate every phase before the first launch
-  if (!c || !q || !w || !z || !o_scratch || n_q <= 0 || n_steps <= 0) return BCA_EINVAL;
-  const int32_t io = c->dtype == BCA_F32 ? BCA_F32 : BCA_BF16;
-  bca_status st = check_append(c, k_new, v_new, n_q, io);
+  bca_status st = check_performer(c, k_new, v_new, q, n_q, w, z, n_ch, n_steps, o_scratch);
   if (st != BCA_OK) return st;
-  const int64_t n_kv = c->n_tokens + n_q;
-  bca_kv_cache after = *c;
-  after.n_tokens = n_kv;
-  st = check_attn(q, n_q, n_kv - n_q, (int32_t)n_q, &after, n_kv, o_scratch, io, io, 0.0f);
-  if (st != BCA_OK) return st;
-  const int32_t kdim = c->n_heads * c->head_dim;
-  const float dtau = 1.0f / (float)n_steps;
-  st = check_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io);
-  if (st != BCA_OK) return st;
-  if (n_q > INT32_MAX) return BCA_EINVAL;
+  return enqueue_performer(c, k_new, v_new, q, n_q, w, z, n_ch, n_steps, o_scratch, workspace,
+                           workspace_bytes, attn_events, s);
+}
 
-  st = enqueue_append(c, k_new, v_new, n_q, s);
+bca_status bca_session_create(bca_kv_cache* c, const int32_t* free_pages, int32_t n_free,
+                              bca_session** out) {
+  if (!out) return BCA_EINVAL;
+  *out = nullptr;
+  bca_status st = check_cache(c);
   if (st != BCA_OK) return st;
-  char* ws = static_cast<char*>(workspace);
-  size_t room = workspace ? workspace_bytes : 0;
-  const size_t eu_bytes = euler_ws_bytes(n_q);
-  const bool eu = room >= eu_bytes;
-  char* attn_ws = room > eu_bytes ? ws + eu_bytes : nullptr;
-  const size_t attn_room = room > eu_bytes ? room - eu_bytes : 0;
-  for (int32_t step = 0; step < n_steps; ++step) {
-    hipEvent_t* ev = attn_events ? attn_events + 3 * step : nullptr;
-    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return BCA_EHIP;
-    st = enqueue_attn(q, n_q, n_kv - n_q, (int32_t)n_q, c, n_kv, o_scratch, io, 0.0f, attn_ws,
-                      attn_room, ev ? ev[1] : nullptr, s);
-    if (st != BCA_OK) return st;
-    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return BCA_EHIP;
-    st = enqueue_euler(z, o_scratch, w, n_q, kdim, n_ch, dtau, io, eu ? ws : nullptr,
-                       eu ? eu_bytes : 0, s);
-    if (st != BCA_OK) return st;
+  if (n_free < 0 || (n_free > 0 && !free_pages)) return BCA_EINVAL;
+  std::vector<bool> seen((size_t)c->n_phys_pages, false);
+  for (int32_t i = 0; i < n_free; ++i) {
+    const int32_t p = free_pages[i];
+    if (p < 0 || p >= c->n_phys_pages || seen[(size_t)p]) return BCA_EINVAL;
+    seen[(size_t)p] = true;
   }
+  bca_session* ss = new (std::nothrow) bca_session;
+  if (!ss) return BCA_EINVAL;
+  ss->cache = c;
+  ss->free_pages.assign(free_pages, free_pages + n_free);
+  ss->next_free = 0;
+  ss->mapped = (c->n_tokens + c->page_size - 1) / c->page_size;
+  ss->exec = nullptr;
+  ss->cap = nullptr;
+  *out = ss;
   return BCA_OK;
+}
+
+bca_status bca_session_unit(bca_session* ss, const void* k_new, const void* v_new, const void* q,
+                            int64_t n_q, const float* w, float* z, int32_t n_ch, int32_t n_steps,
+                            void* o_scratch, void* workspace, size_t workspace_bytes,
+                            int32_t use_graph, hipStream_t s) {
+  if (!ss) return BCA_EINVAL;
+  bca_kv_cache* c = ss->cache;
+  bca_status st = check_performer(c, k_new, v_new, q, n_q, w, z, n_ch, n_steps, o_scratch);
+  if (st != BCA_OK) return st;
+  const int64_t need = (c->n_tokens + n_q + c->page_size - 1) / c->page_size;
+  const int64_t fresh = need > ss->mapped ? need - ss->mapped : 0;
+  if (fresh > (int64_t)(ss->free_pages.size() - ss->next_free)) return BCA_ERANGE;
+
+  // Graphs are captured on the session's own stream (the caller's may be the
+  // null stream, which cannot be captured) and launched on s.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return BCA_EHIP;
+  const bool graph = use_graph && cap == hipStreamCaptureStatusNone;
+  if (graph && !ss->cap && hipStreamCreateWithFlags(&ss->cap, hipStreamNonBlocking) != hipSuccess) {
+    ss->cap = nullptr;
+    return BCA_EHIP;
+  }
+  const hipStream_t ls = graph ? ss->cap : s;   // where the unit's launches are issued
+  const int64_t n_tokens0 = c->n_tokens;
+  hipGraph_t g = nullptr;
+  if (graph && hipStreamBeginCapture(ls, hipStreamCaptureModeRelaxed) != hipSuccess) return BCA_EHIP;
+  hipError_t e = hipSuccess;
+  for (int64_t i = 0; i < fresh && e == hipSuccess; i += kPtBatch) {
+    PtUpdate u{};
+    u.lp0 = (int32_t)(ss->mapped + i);
+    u.count = (int32_t)std::min<int64_t>(kPtBatch, fresh - i);
+    for (int j = 0; j < u.count; ++j) u.phys[j] = ss->free_pages[ss->next_free + (size_t)(i + j)];
+    pt_set_kernel<<<1, kPtBatch, 0, ls>>>(const_cast<int32_t*>(c->page_table), u);
+    e = hipGetLastError();
+  }
+  st = e == hipSuccess ? enqueue_performer(c, k_new, v_new, q, n_q, w, z, n_ch, n_steps, o_scratch,
+                                           workspace, workspace_bytes, nullptr, ls)
+                       : BCA_EHIP;
+  if (graph) {
+    const hipError_t ec = hipStreamEndCapture(ls, &g);
+    if (st == BCA_OK && ec != hipSuccess) st = BCA_EHIP;
+    if (st == BCA_OK) {
+      if (ss->exec) {
+        hipGraphNode_t bad = nullptr;
+        hipGraphExecUpdateResult res;
+        if (hipGraphExecUpdate(ss->exec, g, &bad, &res) != hipSuccess || res != hipGraphExecUpdateSuccess) {
+          // a different shape (new page entries or not, another split
+          // count): instantiate afresh, and clear the refused update from
+          // the thread's last-error state
+          (void)hipGetLastError();
+          (void)hipGraphExecDestroy(ss->exec);
+          ss->exec = nullptr;
+        }
+      }
+      if (!ss->exec && hipGraphInstantiate(&ss->exec, g, nullptr, nullptr, 0) != hipSuccess) {
+        ss->exec = nullptr;
+        st = BCA_EHIP;
+      }
+      if (st == BCA_OK && hipGraphLaunch(ss->exec, s) != hipSuccess) st = BCA_EHIP;
+    }
+    if (g) (void)hipGraphDestroy(g);
+  }
+  if (st != BCA_OK) {
+    c->n_tokens = n_tokens0;                 // nothing of this unit is committed
+    return st;
+  }
+  ss->mapped += fresh;
+  ss->next_free += (size_t)fresh;
+  return BCA_OK;
+}
+
+int64_t bca_session_free_pages(const bca_session* ss) {
+  return ss ? (int64_t)(ss->free_pages.size() - ss->next_free) : -1;
+}
+
+void bca_session_destroy(bca_session* ss) {
+  if (!ss) return;
+  if (ss->exec) (void)hipGraphExecDestroy(ss->exec);
+  if (ss->cap) (void)hipStreamDestroy(ss->cap);
+  delete ss;
 }
 
 }  // extern "C"

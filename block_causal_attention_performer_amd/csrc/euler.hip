@@ -177,9 +177,12 @@ hipError_t launch_euler_proj(const EulerArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const size_t lds = std::max<size_t>((size_t)2 * 16 * (kch + 8) * 2, (size_t)kPWaves * kRows * 16 * 4);
   const dim3 grid((unsigned)((a.n_tok + kRows - 1) / kRows), kEulerChunks);
-  hipError_t e = hipFuncSetAttribute((const void*)euler_proj_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (lds > 65536) {                         // only k above 7936 needs more than the default
+    e = hipFuncSetAttribute((const void*)euler_proj_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   euler_proj_kernel<<<grid, kPWaves * 64, lds, s>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -27,7 +27,10 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library allocates no memory and keeps no global state.
+ *     library allocates no device buffers and keeps no global state.  The
+ *     streaming session (bca_session_*) is the one object the library
+ *     creates: host bookkeeping plus the HIP graph it replays, owned by
+ *     the caller through the session handle.
  *   - Work is enqueued asynchronously on the caller's stream `s`; calls
  *     return after enqueue.  Two calls that share a cache or a workspace
  *     must be ordered by the caller (same stream or events).
@@ -135,8 +138,9 @@ BCA_API bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_n
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   workspace: optional device scratch (may be NULL) of workspace_bytes.
  *        Without it a single kernel with an exact running-maximum softmax
- *        runs.  With it (layout: 64*n_heads*head_dim bytes reserved for
- *        fm_euler_step, then this call's region) a faster kernel runs that
+ *        runs.  With it (layout: 256*n_q bytes, rounded up to a multiple of
+ *        256, reserved for fm_euler_step's partial sums, then this call's
+ *        region) a faster kernel runs that
  *        keeps the first key tile's row maximum as its softmax reference and
  *        flags any query tile whose later logits exceed it by more than
  *        2^40; flagged tiles are recomputed exactly.  The key range may also
@@ -159,11 +163,12 @@ BCA_API bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0,
  *            or BCA_F32), w [k][n_ch] fp32.
  * w == NULL: v = x, x [n_tok][n_ch] fp32 (k ignored).
  * z [n_tok][n_ch] fp32, updated in place.  n_ch <= 64.
- * workspace (may be NULL): with bf16 x, n_ch = 16, k % 32 == 0 and at least
- * 64*k bytes, W is first rewritten into its first 64*k bytes (transposed
- * bf16 high/low halves, W = hi + lo to ~2^-16) and the product runs on the
- * matrix cores; otherwise a slower fp32 vector path runs.  Results do not
- * depend on timing (fixed summation order).
+ * workspace (may be NULL): with bf16 x, n_ch = 16, k a multiple of 256 and
+ * at most 8192, and at least 256*n_tok bytes, the product runs on the
+ * matrix cores (W split into bf16 high/low halves, W = hi + lo to ~2^-16;
+ * eight partial sums per token written to the workspace, then added in
+ * order by a second launch); otherwise a slower fp32 vector path runs.
+ * Results do not depend on timing (fixed summation order).
  */
 BCA_API bca_status fm_euler_step(float* z, const void* x, const float* w,
                          int64_t n_tok, int32_t k, int32_t n_ch, float dtau,
@@ -196,6 +201,44 @@ BCA_API bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void
                           int32_t n_ch, int32_t n_steps, void* o_scratch,
                           void* workspace, size_t workspace_bytes,
                           hipEvent_t* attn_events, hipStream_t s);
+
+/*
+ * Streaming session -- many consecutive performer units over one growing
+ * cache (deep read section 4 step 3: the performer appends every received
+ * slice to its own full-history cache and runs the solver for the next
+ * unit).  The session hands out physical pages as the cache grows: when a
+ * unit's tokens reach logical pages not mapped yet, it takes the next
+ * entries of free_pages, writes them into the cache's page_table on the
+ * stream (before the unit's append), and commits them.  A unit that starts
+ * inside a partly filled page continues that page.
+ *
+ * bca_session_create: c must stay valid for the session's life; the
+ *   logical pages holding c->n_tokens tokens must already be mapped;
+ *   free_pages (host array of n_free distinct physical page ids in
+ *   [0, n_phys_pages), none of them in use) is copied.  Errors: EINVAL.
+ * bca_session_unit: one performer_unit (same arguments and result) after
+ *   the page mapping.  use_graph != 0: the unit's launches are captured on
+ *   s into a HIP graph and replayed (the previous unit's instantiated graph
+ *   is updated in place when its shape allows); on a stream that is
+ *   already being captured the launches simply join that capture.  Errors
+ *   as performer_unit, plus ERANGE when free_pages cannot cover the unit;
+ *   on error nothing of the unit is committed (n_tokens and the page count
+ *   unchanged).
+ * bca_session_free_pages: free pages left (-1 for NULL).
+ * bca_session_destroy: releases the graph and the session (NULL is a no-op);
+ *   the caller must have synchronised s first.
+ * Calls on one session must be ordered by the caller.
+ */
+typedef struct bca_session bca_session;
+BCA_API bca_status bca_session_create(bca_kv_cache* c, const int32_t* free_pages,
+                              int32_t n_free, bca_session** out);
+BCA_API bca_status bca_session_unit(bca_session* ss, const void* k_new, const void* v_new,
+                            const void* q, int64_t n_q, const float* w, float* z,
+                            int32_t n_ch, int32_t n_steps, void* o_scratch,
+                            void* workspace, size_t workspace_bytes, int32_t use_graph,
+                            hipStream_t s);
+BCA_API int64_t bca_session_free_pages(const bca_session* ss);
+BCA_API void bca_session_destroy(bca_session* ss);
 
 /* Workspace size that lets block_causal_attn (n_q queries over n_kv keys of
  * cache c) and fm_euler_step (n_q tokens, k = n_heads*head_dim, n_ch

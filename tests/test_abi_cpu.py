@@ -147,3 +147,40 @@ def test_workspace_bytes_host_only():
     n = bca.lib().bca_workspace_bytes(ctypes.byref(c), 3712, 122496, 16)
     assert n > 3712 * 2 * 128 * 4
     assert bca.lib().bca_workspace_bytes(None, 1, 1, 16) == 0
+
+
+def test_session_create_rejects():
+    L = bca.lib()
+    c = _cache()
+    h = ctypes.c_void_p()
+    for pages, n in (([0, 1, 1], 3), ([0, 4], 2), ([-1], 1)):   # duplicate, out of range, negative
+        arr = (ctypes.c_int32 * len(pages))(*pages)
+        assert L.bca_session_create(ctypes.byref(c), arr, n, ctypes.byref(h)) == -1
+        assert not h.value
+    assert L.bca_session_create(ctypes.byref(c), None, -1, ctypes.byref(h)) == -1
+    assert L.bca_session_create(None, None, 0, ctypes.byref(h)) == -1
+    assert L.bca_session_create(ctypes.byref(c), None, 0, None) == -1
+    assert L.bca_session_free_pages(None) == -1
+    L.bca_session_destroy(None)
+
+
+def test_session_unit_validates_before_mapping():
+    """A unit that the free pages cannot cover returns ERANGE, and a unit with
+    a bad argument EINVAL, before any page is taken or any launch: the
+    session's free-page count and the cache's n_tokens do not move."""
+    L = bca.lib()
+    c = _cache(max_logical_pages=8, n_phys_pages=8, n_tokens=100)   # logical page 0 mapped
+    arr = (ctypes.c_int32 * 2)(5, 6)
+    h = ctypes.c_void_p()
+    assert L.bca_session_create(ctypes.byref(c), arr, 2, ctypes.byref(h)) == 0 and h.value
+    try:
+        assert L.bca_session_free_pages(h) == 2
+        # 100 + 700 tokens reach logical page 3: three new pages, two free
+        st = L.bca_session_unit(h, FAKE, FAKE, FAKE, 700, FAKE, FAKE, 16, 4, FAKE, None, 0, 0, None)
+        assert st == -2 and c.n_tokens == 100 and L.bca_session_free_pages(h) == 2
+        st = L.bca_session_unit(h, FAKE, FAKE, FAKE, 200, FAKE, FAKE, 0, 4, FAKE, None, 0, 0, None)
+        assert st == -1 and c.n_tokens == 100 and L.bca_session_free_pages(h) == 2
+        assert L.bca_session_unit(None, FAKE, FAKE, FAKE, 200, FAKE, FAKE, 16, 4, FAKE, None, 0, 0,
+                                  None) == -1
+    finally:
+        L.bca_session_destroy(h)
