@@ -510,12 +510,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
-#ifndef BCA_ATTN_WIDE
-#define BCA_ATTN_WIDE 0
-#endif
-#ifndef BCA_ATTN_DMA
-#define BCA_ATTN_DMA 1
-#endif
 
 namespace {
 template <int D, int NS>
@@ -556,10 +550,7 @@ int attn_mfma_rows_per_wg() { return BM; }
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done, hipStream_t s) {
   const bool small = a.ps_log2 < 6;
   hipError_t e;
-  if (BCA_ATTN_WIDE && a.head_dim == 128 && !small) {
-    // 64 query rows per wave (same 256-row query tiles, flags and partials)
-    e = launch_attn_wide(a, kv_fp8, s);
-  } else if (BCA_ATTN_DMA && !kv_fp8 && a.head_dim == 128 && !small && a.ps_log2 <= 20) {
+  if (!kv_fp8 && a.head_dim == 128 && !small && a.ps_log2 <= 20) {
     // direct HBM -> LDS tile loads (same query tiles, flags and partials)
     e = launch_attn_dma(a, s);
   } else if (kv_fp8) {

@@ -72,9 +72,6 @@ struct AttnArgs {
 // main_done (may be null) is recorded on s after the main kernel, before
 // the split combine
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done, hipStream_t s);
-// The 64-rows-per-wave kernel behind launch_attn_mfma for head dim 128 and
-// pages of >= 64 keys (same query tiles, flags and split partials).
-hipError_t launch_attn_wide(const AttnArgs& a, bool kv_fp8, hipStream_t s);
 // The bf16 kernel with direct HBM -> LDS tile loads (head dim 128, pages of
 // >= 64 keys); same query tiles, flags and split partials.
 hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t s);
