@@ -34,7 +34,7 @@ UNIT_BUDGET_MS = 160.0
 # sources of the bf16 attention kernel the bench times (direct-load kernel)
 ATTN_KERNEL_SRCS = [os.path.join(ROOT, "block_causal_attention_performer_amd", "csrc", f)
                     for f in ("attn_dma.hip", "attn_common.h")]
-ATTN_KERNEL_NAME = "attn_dma_kernel<128>"
+ATTN_KERNEL_NAME = "attn_dma_kernel<128, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_v02_unit_traffic.txt")
 
 

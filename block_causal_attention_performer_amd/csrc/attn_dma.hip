@@ -71,7 +71,7 @@ __device__ __forceinline__ void wait_vm() {
 
 }  // namespace
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   constexpr int KK = D / 16;                 // k-steps of S^T
   constexpr int DB = D / 32;                 // head-dim blocks of O^T
@@ -79,9 +79,16 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   constexpr int SLOT = BN * D * 2;           // bytes per K or V^T slot
   constexpr int NL = SLOT / (GT * 16);       // direct loads per thread per tile
   static_assert(NL == 4 && RK == 16, "staging layout assumes D = 128");
+  // fp8 cache: tiles of 1-byte codes land in their own rings and are widened
+  // into the bf16 slots by the group that staged them
+  constexpr int SLOT8 = FP8 ? BN * D : 16;   // bytes per fp8 K or V^T slot
+  constexpr int NL8 = FP8 ? SLOT8 / (GT * 16) : 1;
 
   __shared__ __attribute__((aligned(1024))) char lk0[SLOT], lk1[SLOT], lk2[SLOT];
   __shared__ __attribute__((aligned(1024))) char lv0[SLOT], lv1[SLOT], lv2[SLOT];
+  __shared__ __attribute__((aligned(16))) char fk0[SLOT8], fk1[SLOT8], fk2[SLOT8];
+  __shared__ __attribute__((aligned(16))) char fv0[SLOT8], fv1[SLOT8], fv2[SLOT8];
+  __shared__ float scl[2][3];                // fp8: K and V scale of the tile in each slot
   auto kslot = [&](auto r) -> char* {
     if constexpr (decltype(r)::value == 0) return lk0;
     else if constexpr (decltype(r)::value == 1) return lk1;
@@ -98,6 +105,12 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool group_b = wave >= NW / 2;
   const int gw = wave & 3;                   // wave index inside its group
+  auto fslot = [&](auto r) -> char* {        // fp8 ring of this thread's group
+    constexpr int i = decltype(r)::value % 3;
+    if constexpr (i == 0) return group_b ? fv0 : fk0;
+    else if constexpr (i == 1) return group_b ? fv1 : fk1;
+    else return group_b ? fv2 : fk2;
+  };
 
   const int H = a.n_heads;
   const int nqt = (int)((a.n_q + BM - 1) / BM);
@@ -242,13 +255,103 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     }
   };
 
+  // fp8: direct load i of wave gw writes fp8-slot bytes [i*4096 + gw*1024,
+  // +1024), the tile copied as it lies: K as 64 rows of 128 bytes (one run
+  // in the page), V^T as 128 head-dim rows of 64 bytes (row d at d * page
+  // size in the page).  The tile's scale (one per page and head) is read
+  // after the loads, by a vector load so it is counted with them.
+  uint32_t goff8 = 0;
+  int64_t gstep8 = 0;
+  if constexpr (FP8) {
+    if (!group_b) {
+      goff8 = (uint32_t)(gw * 1024 + lane * 16);
+      gstep8 = 4096;
+    } else {
+      const int q0 = gw * 64 + lane;         // chunk q0: row q0 / 4, 16 keys (q0 % 4) * 16 ..
+      goff8 = (uint32_t)(((int64_t)(q0 >> 2) << ps_log2) + (q0 & 3) * 16);
+      gstep8 = (int64_t)64 << ps_log2;
+    }
+  }
+  auto stage8 = [&](int t, char* dst) -> float {
+    const int64_t k0 = (int64_t)t * BN;
+    const int64_t page = page_of(a.page_table, k0 >> ps_log2);
+    const int64_t ph = page * H + h;
+    const char* base = group_b ? vpages + ((ph * D) << ps_log2) + (k0 & psm)
+                               : kpages + (((ph << ps_log2) | (k0 & psm)) * D);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NL8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + gw * 1024 + i * 4096), 16,
+                                               (int)(i * gstep8 + goff8), 0, 0, 0);
+    int si = (int)ph;
+    asm volatile("" : "+v"(si));
+    return (group_b ? a.v_scales : a.k_scales)[si];
+  };
+  // fp8: widen the chunks this thread loaded (fp8 slot `src`) into the
+  // swizzled bf16 slot `dst` (exact: E4M3 fits bf16), zeroing V^T entries
+  // of keys >= n_kv, and publish the tile's scale in scl[group][ss].  K:
+  // chunk q = row q / 8, head dims (q % 8) * 16 .. +15 -> bf16 chunks
+  // 2 (q % 8) and + 1 of that row.  V^T: chunk q = head-dim row q / 4,
+  // keys (q % 4) * 16 .. +15 -> bf16 chunks 2 (q % 4) and + 1.
+  auto widen = [&](int t, const char* src, char* dst, float sc, int ss) {
+    const int gt = tid & (GT - 1);
+    const int64_t k0 = (int64_t)t * BN;
+    const int nvalid = (int)min((int64_t)BN, a.n_kv - k0);
+#pragma unroll
+    for (int i = 0; i < NL8; ++i) {
+      const int q = i * GT + gt;
+      const u32x4 c = *reinterpret_cast<const u32x4*>(src + q * 16);
+      u32x4 lo, hi;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, false));
+        lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, true));
+        hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w + 2], 1.0f, false));
+        hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w + 2], 1.0f, true));
+      }
+      if (!group_b) {
+        const int row = q >> 3, c16 = q & 7;
+        char* rp = dst + row * 256;
+        *reinterpret_cast<u32x4*>(rp + (((2 * c16) ^ swz<16>(row)) * 16)) = lo;
+        *reinterpret_cast<u32x4*>(rp + (((2 * c16 + 1) ^ swz<16>(row)) * 16)) = hi;
+      } else {
+        const int d = q >> 2, c = q & 3;
+        if (nvalid < BN) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int key = 16 * c + 2 * w;
+            if (key >= nvalid) lo[w] &= 0xFFFF0000u;
+            if (key + 1 >= nvalid) lo[w] &= 0x0000FFFFu;
+            if (key + 8 >= nvalid) hi[w] &= 0xFFFF0000u;
+            if (key + 9 >= nvalid) hi[w] &= 0x0000FFFFu;
+          }
+        }
+        char* rp = dst + d * 128;
+        *reinterpret_cast<u32x4*>(rp + (((2 * c) ^ swz<8>(d)) * 16)) = lo;
+        *reinterpret_cast<u32x4*>(rp + (((2 * c + 1) ^ swz<8>(d)) * 16)) = hi;
+      }
+    }
+    if (gt == 0) scl[group_b ? 1 : 0][ss] = sc;
+  };
+
   // ------------------------------------------------------------ main loop
   if (t_begin < t_end) {
     const int t0 = t_begin, tl = t_end - 1;
     // prologue: K(t0), K(t0+1) into K slots 0, 1 (group A); V(t0), V(t0+1)
     // into V slots 0, 1 and zeros into V slot 2, which stands for V(t0-1)
     // (group B); P(t0-1) = 0, so the first PV step adds exact zeros.
-    if (!group_b) {
+    float sc[3] = {1.0f, 1.0f, 1.0f};      // fp8: scale of the tile staged into each slot
+    if constexpr (FP8) {
+      sc[0] = stage8(t0, fslot(ic<0>{}));
+      sc[1] = stage8(min(t0 + 1, tl), fslot(ic<1>{}));
+      if (group_b) {
+        const int gt = tid & (GT - 1);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lv2 + (i * GT + gt) * 16) = u32x4{0, 0, 0, 0};
+      }
+      wait_vm<0>();
+      widen(t0, fslot(ic<0>{}), group_b ? lv0 : lk0, sc[0], 0);   // t0 + 1: in matrix phase t0
+    } else if (!group_b) {
       stage(t0, lk0);
       stage(min(t0 + 1, tl), lk1);
     } else {
@@ -320,12 +423,21 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
         }
       }
       __builtin_amdgcn_s_setprio(0);
+      // fp8: widen tile t+1 (staged one vector phase ago) into its bf16 slot,
+      // which held tile t-2; the matrix group reaches this barrier before
+      // the vector group, so the work fills its wait
+      if constexpr (FP8) {
+        wait_vm<0>();
+        widen(min(t + 1, tl), fslot(ic<r + 1>{}), group_b ? vslot(ic<(r + 1) % 3>{}) : kslot(ic<(r + 1) % 3>{}),
+              sc[(r + 1) % 3], (r + 1) % 3);
+      }
       lds_barrier();
 
       // ---------------- vector phase: next tile two ahead into the free
       // slot, then the softmax of tile t -> P(t)
       const int tn = min(t + 2, tl);
-      if (!group_b) stage(tn, kslot(ic<rp>{}));
+      if constexpr (FP8) sc[(r + 2) % 3] = stage8(tn, fslot(ic<r + 2>{}));
+      else if (!group_b) stage(tn, kslot(ic<rp>{}));
       else stage(tn, vslot(ic<rp>{}));
       if (!idle) {
         const int64_t k0 = (int64_t)t * BN;
@@ -339,7 +451,10 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
               if (key >= lrel) s[mb][rr] = -INFINITY;
             }
         }
-        const float sl = a.scale_log2;
+        // fp8: the K scale of tile t multiplies its logits; its V scale
+        // multiplies P(t) (folded into the exponent), the row sum is
+        // divided by it back
+        const float sl = FP8 ? a.scale_log2 * scl[0][r] : a.scale_log2;
         if (t == t0) {
           float mx = -INFINITY;
 #pragma unroll
@@ -348,7 +463,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
             for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
           m_run = pair_max(mx) * sl;
         }
-        const float mneg = -m_run;
+        const float mneg = FP8 ? __builtin_amdgcn_logf(scl[1][r]) - m_run : -m_run;
         float part[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -362,14 +477,18 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
           }
           part[c] = acc;
         }
-        const float tsum = (part[0] + part[1]) + (part[2] + part[3]);
+        float tsum = (part[0] + part[1]) + (part[2] + part[3]);
+        if constexpr (FP8) tsum *= __builtin_amdgcn_rcpf(scl[1][r]);
         overflow |= !(tsum <= kSlowSum);
         l_run += tsum;
       }
       // publish the tile staged one iteration ago (t+1): wait for its loads
-      // (the NL just issued may stay in flight); group B clears its tail
-      wait_vm<NL>();
-      if (group_b) zero_tail(min(t + 1, tl), vslot(ic<(r + 1) % 3>{}));
+      // (the ones just issued may stay in flight); group B clears its tail
+      // (fp8: tile t+1 was widened and published in the matrix phase)
+      if constexpr (!FP8) {
+        wait_vm<NL>();
+        if (group_b) zero_tail(min(t + 1, tl), vslot(ic<(r + 1) % 3>{}));
+      }
       lds_barrier();
     };
 
@@ -489,8 +608,9 @@ __global__ void attn_sched_reset_kernel(int32_t* sched) {
   if (threadIdx.x < kAttnQueues) sched[threadIdx.x] = 0;
 }
 
-hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn_dma(const AttnArgs& a, bool kv_fp8, hipStream_t s) {
   if (a.head_dim != 128 || a.ps_log2 < 6 || !a.sched) return hipErrorInvalidValue;
+  if (kv_fp8 && (!a.k_scales || !a.v_scales)) return hipErrorInvalidValue;
   if ((int64_t)a.n_heads * ((a.n_q + BM - 1) / BM) * a.nsplit >= (int64_t{1} << 24))
     return hipErrorInvalidValue;             // item numbers must fit 24 bits
   int dev = 0, ncu = 0;
@@ -502,7 +622,8 @@ hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t s) {
   // one persistent workgroup per CU (the LDS rings allow one per CU)
   const unsigned grid = (unsigned)std::min<int64_t>(total, std::max(ncu, 1));
   attn_sched_reset_kernel<<<1, 64, 0, s>>>(a.sched);
-  attn_dma_kernel<128><<<grid, NT, 0, s>>>(a);
+  if (kv_fp8) attn_dma_kernel<128, true><<<grid, NT, 0, s>>>(a);
+  else attn_dma_kernel<128, false><<<grid, NT, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -550,9 +550,9 @@ int attn_mfma_rows_per_wg() { return BM; }
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done, hipStream_t s) {
   const bool small = a.ps_log2 < 6;
   hipError_t e;
-  if (!kv_fp8 && a.head_dim == 128 && !small && a.ps_log2 <= 20) {
+  if (a.head_dim == 128 && !small && a.ps_log2 <= 20) {
     // direct HBM -> LDS tile loads (same query tiles, flags and partials)
-    e = launch_attn_dma(a, s);
+    e = launch_attn_dma(a, kv_fp8, s);
   } else if (kv_fp8) {
     if (a.head_dim != 128 || small) return hipErrorInvalidValue;
     e = launch_t<128, true, false>(a, s);

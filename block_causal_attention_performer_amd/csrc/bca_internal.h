@@ -72,9 +72,10 @@ struct AttnArgs {
 // main_done (may be null) is recorded on s after the main kernel, before
 // the split combine
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipEvent_t main_done, hipStream_t s);
-// The bf16 kernel with direct HBM -> LDS tile loads (head dim 128, pages of
-// >= 64 keys); same query tiles, flags and split partials.
-hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t s);
+// The kernel with direct HBM -> LDS tile loads (head dim 128, pages of >= 64
+// keys; bf16 or fp8 pages, fp8 widened to bf16 in LDS); same query tiles,
+// flags and split partials.
+hipError_t launch_attn_dma(const AttnArgs& a, bool kv_fp8, hipStream_t s);
 // Merge of the split partials into out.
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
 // Exact-rescaling MFMA kernel (no split); with flags set it only rewrites
