@@ -116,3 +116,45 @@ def test_session_v02_units_sampled_rows():
     assert g.n_tokens == w_.n_hist + n_units * lq
     assert g.page_table[n_hist_pages:n_log].cpu().tolist() == perm[n_hist_pages:n_log].tolist()
     ss.close()
+
+
+def test_captured_performer_unit_replays_match_eager():
+    """A caller captures one performer_unit (append + 4 x (attention with the
+    work queues and split combine, Euler with its partial sums)) into a
+    graph on its own stream and replays it three times, with eager work and
+    a synchronisation between replays (z reset, the cache rolled back on the
+    host); every replay must equal the eager unit bit for bit."""
+    say("captured performer_unit replays")
+    H, D, ps, n_hist, n_q, S = 4, 128, 64, 700, 300, 4
+    k = workloads.qkv(31, n_hist + n_q, H, D, 0.5, "bf16").cuda()
+    v = workloads.qkv(32, n_hist + n_q, H, D, 0.5, "bf16").cuda()
+    q = workloads.qkv(33, n_q, H, D, 0.5, "bf16").cuda()
+    w = workloads.randn((H * D, 16), 34).cuda()
+    eps = workloads.randn((n_q, 16), 35).cuda()
+    n_pages = -(-(n_hist + n_q) // ps)
+    pt = torch.randperm(n_pages, generator=torch.Generator().manual_seed(3)).to(torch.int32)
+    g = bca.KVCache(H, D, ps, pt, n_pages, "bf16")
+    bca.kv_append(g, k[:n_hist], v[:n_hist])
+    ws = bca.alloc_workspace(bca.workspace_bytes(g, n_q, n_hist + n_q, 16))
+    osc = torch.empty((n_q, H, D), dtype=torch.bfloat16, device="cuda")
+    z = eps.clone()
+    bca.performer_unit(g, k[n_hist:], v[n_hist:], q, w, z, S, o_scratch=osc, workspace=ws)
+    torch.cuda.synchronize()
+    z_eager, o_eager = z.clone(), osc.clone()
+
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    g.c.n_tokens = n_hist
+    z.copy_(eps)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        bca.performer_unit(g, k[n_hist:], v[n_hist:], q, w, z, S, o_scratch=osc, workspace=ws)
+    for rep in range(3):
+        g.c.n_tokens = n_hist
+        z.copy_(eps)
+        osc.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(z, z_eager), f"replay {rep} z"
+        assert torch.equal(osc, o_eager), f"replay {rep} O"
