@@ -214,13 +214,16 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     goff = (uint32_t)(((int64_t)d << ps_log2) * 2 + (((lane & 7) ^ swz<8>(d)) * 16));
     gstep = (int64_t)32 << ps_log2 << 1;
   }
-  // issue the direct loads of tile t (K for group A, V^T for group B) into `dst`
+  // issue the direct loads of tile t (K for group A, V^T for group B) into
+  // `dst`.  K and V^T pages have the same size; a tile of K starts 2 D bytes
+  // per key into its page, a tile of V^T 2 bytes per key.
+  const int64_t pstride = ((int64_t)H * D << ps_log2) * 2;
+  const char* gbase = (group_b ? vpages : kpages) + (((int64_t)h * D) << ps_log2) * 2;
+  const int kshift = group_b ? 1 : 8;
   auto stage = [&](int t, char* dst) {
     const int64_t k0 = (int64_t)t * BN;
     const int64_t page = page_of(a.page_table, k0 >> ps_log2);
-    const int64_t ph = page * H + h;
-    const char* base = group_b ? vpages + (((ph * D) << ps_log2) + (k0 & psm)) * 2
-                               : kpages + ((((ph << ps_log2) | (k0 & psm)) * D) * 2);
+    const char* base = gbase + page * pstride + ((k0 & psm) << kshift);
     char* l = dst + gw * 1024;
     // raw descriptor over the tile: stride 0, no range limit, gfx9 default
     // data format; lane offsets stay below 2^31 for pages up to 2^20 keys
