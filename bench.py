@@ -157,6 +157,44 @@ def catchup(args, w, inp, cache, hip, stream, bca, workloads):
         "call_pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}), flush=True)
 
 
+def attn_call(args, w, inp, cache, hip, stream, bca):
+    """One streaming block_causal_attn call of the workload's unit (its K/V
+    slice appended first), timed as a whole call: main kernel, split combine
+    and the exact rerun check.  With the v02_share8 workload this is one
+    GPU's share of the v0.2 call under head-sharded context parallelism over
+    8 GPUs (5 of the 40 heads)."""
+    bca.kv_append(cache, inp["k_new"], inp["v_new"])
+    H, D = w.n_heads, w.head_dim
+    ws = bca.alloc_workspace(bca.workspace_bytes(cache, w.unit_tokens, w.n_kv, w.n_ch))
+    out = torch.empty((w.unit_tokens, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        bca.block_causal_attn(inp["q"], cache, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        call()
+    hip.record(e1, stream)
+    ms = hip.elapsed_ms(e0, e1) / args.steps
+    flops = w.attn_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "block-causal attention call TFLOP/s (% MFMA peak)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded device draws, 0.5*N(0,1) Q/K/V rounded to bf16)",
+        "config": {"workload": f"{w.name}_attn", "heads": H, "head_dim": D, "n_q": w.unit_tokens,
+                   "q_pos0": w.n_hist, "block_size": w.unit_tokens, "n_kv": w.n_kv,
+                   "page_size": w.page_size, "parallelism": "none"},
+        "flops_per_call": flops,
+        "call_pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}), flush=True)
+
+
 def stream_units(args, w, inp, bca, workloads):
     """N consecutive performer units through a streaming session starting
     from the workload's history: each unit's pages come from the free list
@@ -224,6 +262,9 @@ def main():
     ap.add_argument("--catchup-units", type=int, default=0,
                     help="instead of the performer step, time one multi-block catch-up "
                          "block_causal_attn call whose queries are the last N units of the cache")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="instead of the performer step, time one block_causal_attn call of the "
+                         "workload's unit (e.g. --workload v02_share8: one GPU's 5-head share)")
     ap.add_argument("--stream-units", type=int, default=0,
                     help="instead of the performer step, stream N consecutive units through a "
                          "session (page allocation, mid-page appends), eager and as HIP graphs")
@@ -251,6 +292,9 @@ def main():
     bca.kv_append(cache, inp["k_hist"], inp["v_hist"])
     if args.catchup_units > 0:
         catchup(args, w, inp, cache, hip, stream, bca, workloads)
+        return
+    if args.attn_only:
+        attn_call(args, w, inp, cache, hip, stream, bca)
         return
     if args.stream_units > 0:
         del cache

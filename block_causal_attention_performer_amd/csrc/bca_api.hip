@@ -1,10 +1,12 @@
 // Host side of the C ABI declared in include/bca.h: argument validation,
 // work-split heuristics and kernel dispatch.  Nothing here allocates device
-// memory or keeps state between calls.
+// memory; the only state kept between calls is a small host-side memo of
+// split decisions.
 #include <math.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -109,11 +111,162 @@ size_t attn_split_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
 // per token] [attention: overflow flags, queue counters, split partials].
 size_t euler_ws_bytes(int64_t n_tok) { return align256((size_t)kEulerChunks * n_tok * 16 * 4); }
 
-// Pick the number of key-range splits: enough workgroups to fill every CU
-// for the last wave without making the partial round trips dominate.
+// Calls that run on the persistent direct-load kernel (its dispatch rule).
+bool attn_persistent(const bca_kv_cache* c) {
+  return c->dtype != BCA_F32 && c->head_dim == 128 && c->page_size >= 64 && c->page_size <= (1 << 20);
+}
+
+// Modelled duration (us) of a persistent attention launch with `s` splits
+// plus its split combine.  The model follows the kernel's scheduling: one
+// workgroup per CU, workgroup i on XCD i % kAttnQueues, kAttnQueues queues
+// holding their heads' items split-major, then head, then query tile; a
+// workgroup takes the next item of its own queue, else of the first later
+// queue with items left.  An item costs its key tiles times the per-tile
+// time of a CU under full load (fewer when its query tile has idle waves)
+// plus a fixed per-item cost; the combine reads s fp32 partials and writes
+// the output at a plain copy's rate.  The constants are measured on MI355X
+// (v0.2 launch: 1.63 us per 64-key tile per CU, about 6 us per item).
+double persistent_cost_us(const std::vector<int64_t>& qt_tiles, const std::vector<double>& qt_frac,
+                          int H, int s, int cus, int64_t n_q, int D) {
+  constexpr double kTileUs = 1.63, kItemUs = 6.0, kCopyBytesPerUs = 4.0e6;
+  const int64_t wsum = 2 * (s - 1) + 1;
+  const int nqt = (int)qt_tiles.size();
+  // cost of the item of split sp and query tile t (equal for every head)
+  std::vector<double> cost_tab((size_t)s * nqt);
+  for (int sp = 0; sp < s; ++sp)
+    for (int t = 0; t < nqt; ++t) {
+      const int64_t T = qt_tiles[t];
+      const int64_t b = T * (2 * sp) / wsum;
+      const int64_t e = sp + 1 == s ? T : T * (2 * sp + 2) / wsum;
+      cost_tab[(size_t)sp * nqt + t] = kItemUs + (double)(e - b) * qt_frac[t] * kTileUs;
+    }
+  // queue x holds heads [lo(x), lo(x+1)): item v is split v / per, query
+  // tile v % nqt, per = its heads x nqt
+  int64_t per[kAttnQueues], len[kAttnQueues], pos[kAttnQueues] = {};
+  int64_t total = 0;
+  for (int x = 0; x < kAttnQueues; ++x) {
+    const int64_t lo = ((int64_t)x * H + kAttnQueues - 1) / kAttnQueues;
+    const int64_t hi = ((int64_t)(x + 1) * H + kAttnQueues - 1) / kAttnQueues;
+    per[x] = (hi - lo) * nqt;
+    len[x] = per[x] * s;
+    total += len[x];
+  }
+  // binary min-heap of (time a workgroup frees, workgroup)
+  const int grid = (int)std::min<int64_t>(total, cus);
+  std::vector<double> ht((size_t)grid, 0.0);
+  std::vector<int> hw((size_t)grid);
+  for (int i = 0; i < grid; ++i) hw[i] = i;
+  int n = grid;
+  double end = 0.0;
+  while (n > 0) {
+    const double t0 = ht[0];
+    const int w = hw[0];
+    int y = -1;
+    for (int k = 0; k < kAttnQueues && y < 0; ++k) {
+      const int x = (w + k) % kAttnQueues;
+      if (pos[x] < len[x]) y = x;
+    }
+    double t_new;
+    int w_new;
+    if (y < 0) {                      // nothing left: the workgroup ends
+      end = std::max(end, t0);
+      --n;
+      if (n == 0) break;
+      t_new = ht[n];
+      w_new = hw[n];
+    } else {
+      const int64_t v = pos[y]++;
+      t_new = t0 + cost_tab[(size_t)(v / per[y]) * nqt + (size_t)(v % nqt)];
+      w_new = w;
+    }
+    // sift the new root down
+    int i = 0;
+    for (;;) {
+      int c = 2 * i + 1;
+      if (c >= n) break;
+      if (c + 1 < n && ht[c + 1] < ht[c]) ++c;
+      if (ht[c] >= t_new) break;
+      ht[i] = ht[c];
+      hw[i] = hw[c];
+      i = c;
+    }
+    ht[i] = t_new;
+    hw[i] = w_new;
+  }
+  const double comb = s == 1 ? 0.0 : ((double)s * n_q * H * D * 4 + (double)n_q * H * D * 2) / kCopyBytesPerUs;
+  return end + comb;
+}
+
+// Split count for the persistent kernel: the modelled best; among counts
+// within 0.75% of it the largest, since finer items also absorb the spread
+// of CU and XCD speeds that the model leaves out.  Decisions are memoised
+// per call shape (one evaluation costs about 1 ms at 40 heads x 15 query
+// tiles).
+int choose_split_persistent(const bca_kv_cache* c, int64_t n_q, int64_t q_pos0, int32_t B, int64_t n_kv,
+                            int max_s, int cus) {
+  struct Memo { int64_t key[7]; int s; };
+  static std::mutex mu;
+  static Memo memo[16];
+  static int n_memo = 0, next_slot = 0;
+  const int64_t key[7] = {c->n_heads, n_q, q_pos0, B, n_kv, max_s, cus};
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < n_memo; ++i)
+      if (!memcmp(memo[i].key, key, sizeof key)) return memo[i].s;
+  }
+  const int64_t BM = attn_mfma_rows_per_wg();
+  const int64_t nqt = (n_q + BM - 1) / BM;
+  std::vector<int64_t> tiles((size_t)nqt);
+  std::vector<double> frac((size_t)nqt);
+  for (int64_t qt = 0; qt < nqt; ++qt) {
+    const int64_t rows = std::min(BM, n_q - qt * BM);
+    const int64_t lim = std::min(n_kv, ((q_pos0 + qt * BM + rows - 1) / B + 1) * (int64_t)B);
+    tiles[qt] = (lim + kKeyTile - 1) / kKeyTile;
+    // a query tile with idle waves: measured 0.87 of a full tile's time
+    // with half of its 8 waves idle
+    frac[qt] = 0.74 + 0.26 * (double)((rows + 31) / 32) / 8.0;
+  }
+  // as for the register-staged kernels: at least 4 key tiles per split on
+  // average
+  double mean_tiles = 0.0;
+  for (int64_t t : tiles) mean_tiles += (double)t;
+  mean_tiles /= (double)nqt;
+  while (max_s > 1 && mean_tiles / max_s < 4.0) --max_s;
+  std::vector<double> cost((size_t)max_s + 1);
+  double best = 1e300;
+  for (int s = 1; s <= max_s; ++s) {
+    cost[s] = persistent_cost_us(tiles, frac, c->n_heads, s, cus, n_q, c->head_dim);
+    best = std::min(best, cost[s]);
+  }
+  int pick = 1;
+  for (int s = 1; s <= max_s; ++s)
+    if (cost[s] <= 1.0075 * best) pick = s;
+  std::lock_guard<std::mutex> g(mu);
+  Memo& m = memo[next_slot];
+  memcpy(m.key, key, sizeof key);
+  m.s = pick;
+  next_slot = (next_slot + 1) % 16;
+  n_memo = std::min(n_memo + 1, 16);
+  return pick;
+}
+
+// Pick the number of key-range splits.  Persistent kernel with at most 4
+// (query tile, head) pairs per CU: from the model above, where the end of
+// the launch (a few items per CU) decides.  Otherwise (more pairs, or the
+// register-staged kernels with one workgroup per item): enough workgroups
+// to fill every CU for the last wave without making the partial round
+// trips dominate; with many items per CU the two agree (both pick 4 splits
+// for 8 v0.2 units of queries at once).
 int choose_attn_split(const bca_kv_cache* c, int64_t n_q, int64_t q_pos0, int32_t B, int64_t n_kv,
                       size_t room) {
   if (c->dtype == BCA_F32) return 1;
+  const int cus = cu_count();
+  if (attn_persistent(c) &&
+      ((n_q + attn_mfma_rows_per_wg() - 1) / attn_mfma_rows_per_wg()) * c->n_heads <= 4 * (int64_t)cus) {
+    int max_s = 1;
+    while (max_s < kMaxAttnSplit && attn_split_bytes(c, n_q, max_s + 1) <= room) ++max_s;
+    return choose_split_persistent(c, n_q, q_pos0, B, n_kv, max_s, cus);
+  }
   const int64_t BM = attn_mfma_rows_per_wg();
   const int64_t nqt = (n_q + BM - 1) / BM;
   double tiles = 0.0;
@@ -124,7 +277,6 @@ int choose_attn_split(const bca_kv_cache* c, int64_t n_q, int64_t q_pos0, int32_
   }
   tiles /= (double)nqt;
   const double wgs = (double)nqt * c->n_heads;
-  const int cus = cu_count();
   int best = 1;
   double best_cost = 1e300;
   for (int s = 1; s <= kMaxAttnSplit; ++s) {

@@ -68,6 +68,23 @@ def test_v02_attention_sampled_rows():
     assert_close(got, want, 2e-2, 1e-2, what="v0.2 O sampled rows")
 
 
+def test_v02_share8_attention_sampled_rows():
+    """One GPU's share of the v0.2 call under head-sharded context
+    parallelism over 8 GPUs (5 x 128 heads, the same 3712 queries over
+    122,496 keys), as `bench.py --workload v02_share8 --attn-only` times it:
+    few (query tile, head) pairs, so the split count comes from the
+    scheduler model (7 splits on 256 CUs).  More sampled rows, all heads."""
+    say("v0.2 one-GPU head share (5 heads)")
+    w, inp, g, ws = _setup("v02_share8")
+    bca.kv_append(g, inp["k_new"], inp["v_new"])
+    out = bca.block_causal_attn(inp["q"], g, workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([ROWS, np.arange(0, 3712, 97), np.arange(3584, 3712, 13)]))
+    want = _oracle_rows(w, inp, rows)
+    got = out[rows.tolist()].float().cpu().numpy()
+    assert_close(got, want, 2e-2, 1e-2, what="v0.2 share O sampled rows")
+
+
 def test_v02_attention_peaky_planted():
     """Sharp-softmax v0.2 variant: Q and K x4 (logit std ~4) and keys equal
     to chosen queries planted in the first page, at a page boundary, deep in

@@ -16,6 +16,9 @@ alwayszhang.cn deep read, section 3.3):
                current slice pre-appended, one attention call
   v02_unit     v02 shapes, append + 4 x (attention + Euler), W 5120x16
   v02_long_fp8 v02 unit over 750 history units in an fp8-e4m3 cache
+  v02_share8   one GPU's head share of the v02 attention call under
+               head-sharded (Ulysses) context parallelism over 8 GPUs:
+               5 x 128, the same 3712 queries over 122,496 keys
 
 Draw recipe: every tensor has its own sub-stream, seed = 1000*cfg_index +
 slot, slots in the order Q, K_hist, V_hist, K_new, V_new, eps, z0, W.
@@ -87,6 +90,7 @@ WORKLOADS = {
     "v02_attn": Workload("v02_attn", 2, "bf16", 40, 128, 3712, 32, 0.5),
     "v02_unit": Workload("v02_unit", 3, "bf16", 40, 128, 3712, 32, 0.5),
     "v02_long_fp8": Workload("v02_long_fp8", 4, "fp8", 40, 128, 3712, 750, 0.5),
+    "v02_share8": Workload("v02_share8", 5, "bf16", 5, 128, 3712, 32, 0.5),
 }
 
 
