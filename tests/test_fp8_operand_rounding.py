@@ -1,0 +1,88 @@
+"""Why attention over an fp8 cache keeps its MFMA operands Q and P in bf16.
+
+gfx950's fp8 MFMAs would need Q (for S = K Q^T) and the softmax weights P
+(for O = P V) in E4M3 as well.  Rounding either to 3 mantissa bits costs far
+more than the cache's own quantisation: these CPU checks round them with the
+oracle's E4M3 encoder, on the workloads' distribution (Q, K, V ~ 0.5 N(0,1),
+head dim 128, K/V stored as E4M3 codes with one scale per block), and
+compare with the oracle's attention over the same dequantised K/V.  The bar
+is the fp8 attention tests' relative RMS of 1e-2:
+
+* E4M3 P exceeds it even with the exact row maximum as reference (≈2.7e-2):
+  the output is a near-cancelling average of many values, so per-weight
+  rounding of 2^-4 shows almost undamped.
+* E4M3 Q stays under it at logit std 0.25 (≈6e-3, most of the budget), but
+  not once the softmax is sharp (Q and K x4: ≈5e-2).
+* Q as a sum of two E4M3 terms (high part, then the rounded remainder) is
+  as accurate as bf16 Q (1.4e-3 against 3.6e-3 for rounding the sharp case's
+  fp32 Q to bf16), but then S needs two fp8 MFMAs, as many cycles as one
+  bf16 MFMA pass, so the fp8 rate buys nothing.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+REL = 1e-2      # relative RMS bar of the fp8 attention tests
+D = 128
+
+
+def _rel_rms(got, want):
+    d = np.asarray(got) - np.asarray(want)
+    return float(np.sqrt(np.mean(d * d)) / np.sqrt(np.mean(np.asarray(want) ** 2)))
+
+
+def _fp8_rows(x):
+    """Each row through the cache's quantiser (scale amax/448), dequantised."""
+    out = np.empty_like(x, dtype=np.float64)
+    for i in range(x.shape[0]):
+        codes, scale = oracle.quantize_rows(x[i:i + 1])
+        out[i] = oracle.e4m3_decode(codes)[0] * np.float64(scale)
+    return out
+
+
+def _fp8_block(x):
+    codes, scale = oracle.quantize_rows(x)
+    return oracle.e4m3_decode(codes) * np.float64(scale)
+
+
+def _setup(seed, n_kv=4096, n_q=48, factor=1.0):
+    rng = np.random.default_rng(seed)
+    q = (rng.standard_normal((n_q, D)) * 0.5 * factor).astype(np.float32)
+    k = (rng.standard_normal((n_kv, D)) * 0.5 * factor).astype(np.float32)
+    v = (rng.standard_normal((n_kv, D)) * 0.5).astype(np.float32)
+    kd, vd = _fp8_block(k), _fp8_block(v)
+    want = oracle.attention_dense(q[:, None], kd[:, None], vd[:, None])[:, 0]
+    return q, kd, vd, want
+
+
+def test_fp8_p_exceeds_tolerance():
+    q, kd, vd, want = _setup(1)
+    s = (q.astype(np.float64) @ kd.T) / np.sqrt(D)
+    p = np.exp(s - s.max(axis=1, keepdims=True))          # in (0, 1], exact reference
+    off = 2.0 ** 6                                        # keeps small weights out of subnormals
+    p8 = oracle.e4m3_decode(oracle.e4m3_encode((p * off).astype(np.float32))) / off
+    got = (p8 @ vd) / p8.sum(axis=1, keepdims=True)
+    # the same arithmetic without the rounding reproduces the oracle
+    assert _rel_rms((p @ vd) / p.sum(axis=1, keepdims=True), want) < 1e-12
+    assert _rel_rms(got, want) > 2 * REL
+
+
+def test_fp8_q_within_tolerance_only_for_flat_softmax():
+    q, kd, vd, want = _setup(2)
+    flat = _rel_rms(oracle.attention_dense(_fp8_rows(q)[:, None], kd[:, None], vd[:, None])[:, 0], want)
+    assert 0.3 * REL < flat < REL
+    q, kd, vd, want = _setup(3, factor=4.0)
+    sharp = _rel_rms(oracle.attention_dense(_fp8_rows(q)[:, None], kd[:, None], vd[:, None])[:, 0], want)
+    assert sharp > 3 * REL
+
+
+def test_two_term_fp8_q_matches_bf16_accuracy():
+    q, kd, vd, want = _setup(3, factor=4.0)
+    hi = _fp8_rows(q)
+    lo = _fp8_rows((q - hi).astype(np.float32))
+    two = _rel_rms(oracle.attention_dense((hi + lo)[:, None], kd[:, None], vd[:, None])[:, 0], want)
+    q_bf16 = torch.from_numpy(q).to(torch.bfloat16).double().numpy()
+    bf16 = _rel_rms(oracle.attention_dense(q_bf16[:, None], kd[:, None], vd[:, None])[:, 0], want)
+    # no worse than rounding Q to bf16 (the storage format of the queries)
+    assert two <= bf16
