@@ -51,10 +51,7 @@ constexpr int NW = 8;             // waves per workgroup (two groups of four)
 constexpr int NT = NW * 64;
 constexpr int GT = NT / 2;        // threads per group
 constexpr int BM = NW * QW;       // query rows per workgroup
-#ifndef BCA_ATTN_NIF
-#define BCA_ATTN_NIF 6
-#endif
-constexpr int NIF = BCA_ATTN_NIF; // LDS reads kept in flight ahead of the MFMAs
+constexpr int NIF = 6;            // LDS reads kept in flight ahead of the MFMAs
 static_assert(NW == kAttnFlagWaves, "one overflow flag per wave");
 
 }  // namespace

@@ -519,7 +519,7 @@ bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t
   bca_status st = check_attn(q, n_q, q_pos0, block_size, c, n_kv, out, q_dtype, out_dtype,
                              softmax_scale);
   if (st != BCA_OK) return st;
-  // the attention region follows the Euler region (W's transposed halves)
+  // the attention region follows the velocity projection's partial sums
   char* ws = static_cast<char*>(workspace);
   size_t room = workspace_bytes;
   if (ws) {

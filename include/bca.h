@@ -138,9 +138,11 @@ BCA_API bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_n
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   workspace: optional device scratch (may be NULL) of workspace_bytes.
  *        Without it a single kernel with an exact running-maximum softmax
- *        runs.  With it (layout: 256*n_q bytes, rounded up to a multiple of
+ *        runs.  With it (layout: 512*n_q bytes, rounded up to a multiple of
  *        256, reserved for fm_euler_step's partial sums, then this call's
- *        region) a faster kernel runs that
+ *        region: overflow flags, 256 bytes of work-queue counters that the
+ *        call zeroes itself, the fp32 split partials) a faster kernel runs
+ *        that
  *        keeps the first key tile's row maximum as its softmax reference and
  *        flags any query tile whose later logits exceed it by more than
  *        2^40; flagged tiles are recomputed exactly.  The key range may also
@@ -164,7 +166,7 @@ BCA_API bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0,
  * w == NULL: v = x, x [n_tok][n_ch] fp32 (k ignored).
  * z [n_tok][n_ch] fp32, updated in place.  n_ch <= 64.
  * workspace (may be NULL): with bf16 x, n_ch = 16, k a multiple of 256 and
- * at most 8192, and at least 256*n_tok bytes, the product runs on the
+ * at most 8192, and at least 512*n_tok bytes, the product runs on the
  * matrix cores (W split into bf16 high/low halves, W = hi + lo to ~2^-16;
  * eight partial sums per token written to the workspace, then added in
  * order by a second launch); otherwise a slower fp32 vector path runs.

@@ -137,6 +137,43 @@ def test_split_kv_matches_single_pass():
     assert torch.equal(b, c)
 
 
+def _split_ws_bytes(n_q, H, D, s):
+    """Workspace bytes that hold block_causal_attn's region for at most s
+    key-range splits: 512 bytes per query for fm_euler_step first, then the
+    overflow flags (one int32 per 256-row query tile, head, split and wave
+    of 8), 256 bytes of queue counters and, for s > 1, the fp32 partials
+    O [s][n_q][H][D] and (m, l) [s][n_q][H][2], each part 256-aligned."""
+    a = lambda x: -(-x // 256) * 256
+    flags = a(-(-n_q // 256) * H * s * 8 * 4)
+    parts = a(s * n_q * H * D * 4) + a(s * n_q * H * 2 * 4) if s > 1 else 0
+    return a(512 * n_q) + flags + 256 + parts
+
+
+def test_every_split_count():
+    """A shape with 2 (query tile, head) pairs, where every extra split adds
+    parallelism, so a workspace that fits the partials of at most s splits
+    runs exactly s of them: s = 1 .. 8 (the merge kernel for every count)
+    all match the oracle, are deterministic and differ from one another
+    bitwise (each count rounds differently)."""
+    H, D, n_kv, n_q = 2, 128, 6000, 256
+    q, k, v, g, _ = _bf16_case(H, D, n_kv, 256, 2, 93)
+    qq = q[n_kv - n_q:].cuda()
+    want = oracle.attention_dense(q[n_kv - n_q:].double().numpy(), k.double().numpy(),
+                                  v.double().numpy(), n_kv - n_q, n_q)
+    outs = []
+    for s in range(1, 9):
+        ws = bca.alloc_workspace(_split_ws_bytes(n_q, H, D, s))
+        a = bca.block_causal_attn(qq, g, workspace=ws)
+        b = bca.block_causal_attn(qq, g, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        assert_close(np64(a), want, BF16_TOL, BF16_REL, what=f"{s} splits")
+        outs.append(a)
+    for i in range(8):
+        for j in range(i):
+            assert not torch.equal(outs[i], outs[j]), (i + 1, j + 1)
+
+
 @pytest.mark.parametrize("ws", [False, True])
 def test_bitwise_invariants(ws):
     """P5 shuffled page table, P7 garbage appended past n_kv, determinism."""
