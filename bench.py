@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "block-causal attn TFLOP/s (% MFMA peak) + ms/160ms-unit at v0.2 shapes"
+METRIC_WORKLOAD = "v02_unit"  # the workload METRIC names; other workloads get their own label
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 UNIT_BUDGET_MS = 160.0
@@ -35,7 +36,7 @@ UNIT_BUDGET_MS = 160.0
 ATTN_KERNEL_SRCS = [os.path.join(ROOT, "block_causal_attention_performer_amd", "csrc", f)
                     for f in ("attn_dma.hip", "attn_common.h")]
 ATTN_KERNEL_NAME = "attn_dma_kernel<128, false>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_v02_unit_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_v02_unit_traffic.txt")   # v02_unit launches
 
 
 class Hip:
@@ -72,7 +73,7 @@ def _kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(flops_unit_bytes=None):
+def _traffic():
     """HBM bytes per attention launch from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel source; else None."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -114,7 +115,7 @@ def cpu_baseline(inp, w, rows_n, heads_n):
     flops = 4.0 * w.head_dim * len(rows) * len(heads) * w.n_kv
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"attention_dense (float64 numpy) of {len(rows)} query rows x {len(heads)} "
-                      f"heads over all {w.n_kv} keys of the v0.2 unit; {dt:.2f} s",
+                      f"heads over all {w.n_kv} keys of the {w.name} workload's unit; {dt:.2f} s",
             "seconds": dt}
 
 
@@ -162,7 +163,8 @@ def attn_call(args, w, inp, cache, hip, stream, bca):
     slice appended first), timed as a whole call: main kernel, split combine
     and the exact rerun check.  With the v02_share8 workload this is one
     GPU's share of the v0.2 call under head-sharded context parallelism over
-    8 GPUs (5 of the 40 heads)."""
+    8 GPUs (5 of the 40 heads); with v02_long_fp8, the call over 750 units
+    of fp8 history (the MFMAs stay bf16)."""
     bca.kv_append(cache, inp["k_new"], inp["v_new"])
     H, D = w.n_heads, w.head_dim
     ws = bca.alloc_workspace(bca.workspace_bytes(cache, w.unit_tokens, w.n_kv, w.n_ch))
@@ -190,7 +192,7 @@ def attn_call(args, w, inp, cache, hip, stream, bca):
         "data": "synthetic (seeded device draws, 0.5*N(0,1) Q/K/V rounded to bf16)",
         "config": {"workload": f"{w.name}_attn", "heads": H, "head_dim": D, "n_q": w.unit_tokens,
                    "q_pos0": w.n_hist, "block_size": w.unit_tokens, "n_kv": w.n_kv,
-                   "page_size": w.page_size, "parallelism": "none"},
+                   "page_size": w.page_size, "kv_cache": w.dtype, "parallelism": "none"},
         "flops_per_call": flops,
         "call_pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}), flush=True)
 
@@ -366,8 +368,9 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    metric = METRIC if w.name == METRIC_WORKLOAD else METRIC.replace("v0.2 shapes", f"{w.name} shapes")
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -391,7 +394,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(), "kernel": ATTN_KERNEL_NAME,
+                     "traffic": _traffic() if w.name == METRIC_WORKLOAD else None,
+                     "kernel": ATTN_KERNEL_NAME,
                      "avg_launch_ms": round(attn_avg, 4), "flops_per_launch": flops_call},
         "kernels": {
             "kv_append": {"median_ms": round(app_med, 5), "bytes": app_bytes,
