@@ -185,6 +185,9 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
   bool overflow = false;
+  // bf16: running row sums of the lane's keys, one per 16-key chunk of a
+  // tile, added up once at the end of the item
+  float lc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // per-lane LDS read addresses: chunk j of the lane's row at row + ((16 j) ^ x)
   const int kr = sigma32(col);
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int mb = c >> 1, rb = 8 * (c & 1);
-          float acc = 0.0f;
+          float acc = FP8 ? 0.0f : lc[c];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
@@ -480,10 +483,16 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
           }
           part[c] = acc;
         }
-        float tsum = (part[0] + part[1]) + (part[2] + part[3]);
-        if constexpr (FP8) tsum *= __builtin_amdgcn_rcpf(scl[1][r]);
-        overflow |= !(tsum <= kSlowSum);
-        l_run += tsum;
+        if constexpr (FP8) {
+          // the tile's own V scale divides its sum back out
+          float tsum = (part[0] + part[1]) + (part[2] + part[3]);
+          tsum *= __builtin_amdgcn_rcpf(scl[1][r]);
+          overflow |= !(tsum <= kSlowSum);
+          l_run += tsum;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) lc[c] = part[c];
+        }
       }
       // publish the tile staged one iteration ago (t+1): wait for its loads
       // (the ones just issued may stay in flight); group B clears its tail
@@ -526,6 +535,12 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
   }
 
+  if constexpr (!FP8) {
+    // bf16: the whole sum against the bound (any tile's sum above it puts
+    // the total above it too)
+    l_run = (lc[0] + lc[1]) + (lc[2] + lc[3]);
+    overflow |= !(l_run <= kSlowSum);
+  }
   // one flag per (query tile, split, wave), written unconditionally
   const bool wave_overflow = __builtin_amdgcn_ballot_w64(overflow) != 0;
   if (lane == 0) a.flags_out[((int64_t)(h * nqt + qt) * a.nsplit + split) * NW + wave] = wave_overflow;

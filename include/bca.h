@@ -142,10 +142,10 @@ BCA_API bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_n
  *        256, reserved for fm_euler_step's partial sums, then this call's
  *        region: overflow flags, 256 bytes of work-queue counters that the
  *        call zeroes itself, the fp32 split partials) a faster kernel runs
- *        that
- *        keeps the first key tile's row maximum as its softmax reference and
- *        flags any query tile whose later logits exceed it by more than
- *        2^40; flagged tiles are recomputed exactly.  The key range may also
+ *        that keeps the first key tile's row maximum as its softmax
+ *        reference and flags any query tile in which a row's weights
+ *        relative to that reference add up past 2^40 or to a non-finite
+ *        value; flagged tiles are recomputed exactly.  The key range may also
  *        be split across workgroups and merged by a fixed-order log-sum-exp
  *        combine.  Results never depend on timing.  bca_workspace_bytes()
  *        gives the size that enables every path.
