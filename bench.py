@@ -356,11 +356,28 @@ def main():
         bca.fm_euler_step(z, osc, inp["w"], 1.0 / S, workspace=ws)
         hip.record(e1, stream)
         eul_ms.append(hip.elapsed_ms(e0, e1))
-    del flush
     app_bytes = 2 * 2 * lq * H * D * 2            # read + write, K and V
     eul_bytes = lq * H * D * 2 + H * D * 16 * 4 + 2 * lq * 16 * 4
     app_med = sorted(app_ms)[len(app_ms) // 2]
     eul_med = sorted(eul_ms)[len(eul_ms) // 2]
+
+    # the ceiling at these sizes: a plain device copy (torch) moving the
+    # same number of bytes (half read, half written), timed the same way
+    def copy_gbps(moved):
+        src = torch.empty(moved // 2, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        ms = []
+        for _ in range(args.kernel_reps):
+            flush.sum()
+            hip.record(e0, stream)
+            dst.copy_(src)
+            hip.record(e1, stream)
+            ms.append(hip.elapsed_ms(e0, e1))
+        return moved / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e9
+
+    app_copy = copy_gbps(app_bytes)
+    eul_copy = copy_gbps(eul_bytes)
+    del flush
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -400,10 +417,14 @@ def main():
         "kernels": {
             "kv_append": {"median_ms": round(app_med, 5), "bytes": app_bytes,
                           "GBps": round(app_bytes / (app_med * 1e-3) / 1e9, 1),
-                          "hbm_frac": round(app_bytes / (app_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                          "hbm_frac": round(app_bytes / (app_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "same_size_copy_GBps": round(app_copy, 1),
+                          "frac_of_same_size_copy": round(app_bytes / (app_med * 1e-3) / 1e9 / app_copy, 3)},
             "fm_euler_step": {"median_ms": round(eul_med, 5), "bytes": eul_bytes,
                               "GBps": round(eul_bytes / (eul_med * 1e-3) / 1e9, 1),
-                              "hbm_frac": round(eul_bytes / (eul_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                              "hbm_frac": round(eul_bytes / (eul_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "same_size_copy_GBps": round(eul_copy, 1),
+                              "frac_of_same_size_copy": round(eul_bytes / (eul_med * 1e-3) / 1e9 / eul_copy, 3)},
         },
     }
     if not args.no_cpu_baseline:
