@@ -62,3 +62,30 @@ def test_f32_projection_generic():
     bca.fm_euler_step(zg, x.cuda(), w.cuda(), 0.25)
     want = z.double().numpy() - 0.25 * oracle.velocity(x.double().numpy(), w.double().numpy())
     assert_close(np64(zg), want, 1e-5, what="f32 projection")
+
+
+def test_projection_workspace_contents_do_not_matter():
+    """The projection's k-part sums are written whole before they are read,
+    so any initial workspace contents work: a workspace of random bytes, of
+    all-ones bytes and a reused one give the same z bit for bit, call after
+    call (ragged last row block: 1000 tokens)."""
+    n_tok, H, D = 1000, 40, 128
+    x = workloads.qkv(13, n_tok, H, D, 0.05, "bf16").reshape(n_tok, H * D).cuda()
+    w = workloads.randn((H * D, 16), 14).cuda()
+    z0 = workloads.randn((n_tok, 16), 15).cuda()
+    nbytes = -(-n_tok * 512 // 256) * 256
+    g = torch.Generator(device="cuda").manual_seed(16)
+    junk = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    ones = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    ref = None
+    for ws in (junk, ones, junk, junk):
+        z = z0.clone()
+        bca.fm_euler_step(z, x, w, 0.25, workspace=ws)
+        bca.fm_euler_step(z, x, w, 0.25, workspace=ws)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = z.clone()
+            want = z0.double().cpu().numpy() - 0.5 * oracle.velocity(
+                x.double().cpu().numpy().reshape(n_tok, H, D), w.double().cpu().numpy())
+            assert_close(np64(z), want, 2e-2, what="two steps from a junk workspace")
+        assert torch.equal(z, ref)
