@@ -188,7 +188,8 @@ def attn_call(args, w, inp, cache, hip, stream, bca):
         "metric": "block-causal attention call TFLOP/s (% MFMA peak)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 S (Q as two e4m3 terms), bf16 PV" if w.dtype == "fp8" else "bf16",
         "data": "synthetic (seeded device draws, 0.5*N(0,1) Q/K/V rounded to bf16)",
         "config": {"workload": f"{w.name}_attn", "heads": H, "head_dim": D, "n_q": w.unit_tokens,
                    "q_pos0": w.n_hist, "block_size": w.unit_tokens, "n_kv": w.n_kv,

@@ -1,6 +1,7 @@
-// Block-causal attention over the paged KV cache: bf16 MFMA kernel whose
-// K / V^T tiles move HBM -> LDS by direct 16-byte LDS loads (gfx950
-// buffer_load_dwordx4 ... lds), head dim 128, pages of >= 64 keys.
+// Block-causal attention over the paged KV cache: MFMA kernel whose K / V^T
+// tiles move HBM -> LDS by direct 16-byte LDS loads (gfx950
+// buffer_load_dwordx4 ... lds), head dim 128, pages of >= 64 keys; bf16
+// pages, or fp8 pages with S on the fp8 MFMA and PV in bf16.
 //
 // Visibility (explainer "wan-streamer-realtime-av", listening-while-speaking
 // section and its figure caption; youleyou.com article section 3.1): query
@@ -79,8 +80,9 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   constexpr int SLOT = BN * D * 2;           // bytes per K or V^T slot
   constexpr int NL = SLOT / (GT * 16);       // direct loads per thread per tile
   static_assert(NL == 4 && RK == 16, "staging layout assumes D = 128");
-  // fp8 cache: tiles of 1-byte codes land in their own rings and are widened
-  // into the bf16 slots by the group that staged them
+  // fp8 cache: tiles of 1-byte codes land in their own rings; K is read
+  // from its ring by the fp8 MFMA, V^T is widened into the bf16 slots by
+  // group B
   constexpr int SLOT8 = FP8 ? BN * D : 16;   // bytes per fp8 K or V^T slot
   constexpr int NL8 = FP8 ? SLOT8 / (GT * 16) : 1;
 
@@ -105,6 +107,12 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool group_b = wave >= NW / 2;
   const int gw = wave & 3;                   // wave index inside its group
+  auto k8slot = [&](auto r) -> char* {       // fp8 K ring (read by both groups)
+    constexpr int i = decltype(r)::value % 3;
+    if constexpr (i == 0) return fk0;
+    else if constexpr (i == 1) return fk1;
+    else return fk2;
+  };
   auto fslot = [&](auto r) -> char* {        // fp8 ring of this thread's group
     constexpr int i = decltype(r)::value % 3;
     if constexpr (i == 0) return group_b ? fv0 : fk0;
@@ -172,12 +180,57 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   const bool idle = r0 + wave * QW >= a.n_q;
 
   bf16x8 qf[KK];
-  {
+  // fp8 cache: S = K Q^T runs on the fp8 MFMA with the K codes as they lie
+  // in LDS and Q as two E4M3 terms on one scale per query row,
+  // Q = qs (hi + lo) with hi = E4M3(Q/qs), lo = E4M3(Q/qs - hi), qs =
+  // amax/448: as accurate as the bf16 Q itself.  Lane (half, col) holds
+  // dims 64 kk + 32 half + [0, 32) of query col, the B operand of
+  // v_mfma_scale_f32_32x32x64_f8f6f4 (its K fragments cover the same dims
+  // in the same byte order).
+  i32x8 qh[2], ql[2];
+  float qs = 1.0f;
+  if constexpr (!FP8) {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow * H + h) * D + 8 * half;
     const bool ok = qrow < a.n_q;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(qp + 16 * kk) : u32x4{0, 0, 0, 0});
+  } else {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow * H + h) * D + 32 * half;
+    const bool ok = qrow < a.n_q;
+    u32x4 qv[2][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        qv[kk][p] = ok ? ld16(qp + 64 * kk + 8 * p) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(qv[kk][p][w] << 16)),
+                                   fabsf(__uint_as_float(qv[kk][p][w] & 0xFFFF0000u))));
+      }
+    amax = pair_max(amax);
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    qs = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {     // 4 dims per code word
+          const uint32_t u0 = qv[kk][p][2 * w2], u1 = qv[kk][p][2 * w2 + 1];
+          const float y0 = __uint_as_float(u0 << 16) * inv, y1 = __uint_as_float(u0 & 0xFFFF0000u) * inv;
+          const float y2 = __uint_as_float(u1 << 16) * inv, y3 = __uint_as_float(u1 & 0xFFFF0000u) * inv;
+          int hw = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+          hw = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, hw, true);
+          const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+          const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+          int lw = __builtin_amdgcn_cvt_pk_fp8_f32(y0 - d01[0], y1 - d01[1], 0, false);
+          lw = __builtin_amdgcn_cvt_pk_fp8_f32(y2 - d23[0], y3 - d23[1], lw, true);
+          qh[kk][2 * p + w2] = hw;
+          ql[kk][2 * p + w2] = lw;
+        }
   }
 
   f32x16 o[DB];
@@ -193,6 +246,8 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   const int kr = sigma32(col);
   const uint32_t krow = (uint32_t)(kr * D * 2), kx = (uint32_t)((swz<RK>(kr) ^ half) * 16);
   const uint32_t vrow = (uint32_t)(kr * BN * 2), vx = (uint32_t)((swz<8>(kr) ^ half) * 16);
+  // fp8 K rows of 128 bytes: lane reads chunks 4 kk + 2 half (+1) of row kr
+  const uint32_t krow8 = (uint32_t)(kr * 128), kx8 = (uint32_t)(((2 * half) ^ swz<8>(kr)) * 16);
 
   const int ps_log2 = a.ps_log2;
   const int psm = (1 << ps_log2) - 1;
@@ -262,15 +317,18 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   };
 
   // fp8: direct load i of wave gw writes fp8-slot bytes [i*4096 + gw*1024,
-  // +1024), the tile copied as it lies: K as 64 rows of 128 bytes (one run
-  // in the page), V^T as 128 head-dim rows of 64 bytes (row d at d * page
-  // size in the page).  The tile's scale (one per page and head) is read
+  // +1024): K as 64 rows of 128 bytes (one run in the page) with their
+  // 16-byte chunks swizzled for the fp8 MFMA's reads, V^T as 128 head-dim
+  // rows of 64 bytes (row d at d * page size in the page) as they lie.  The tile's scale (one per page and head) is read
   // after the loads, by a vector load so it is counted with them.
   uint32_t goff8 = 0;
   int64_t gstep8 = 0;
   if constexpr (FP8) {
     if (!group_b) {
-      goff8 = (uint32_t)(gw * 1024 + lane * 16);
+      // 16-byte chunk c of K row r at position c ^ swz8(r) (the swizzle
+      // depends on r's low 4 bits, so load i is rows + 32 i at a uniform step)
+      const int row = gw * 8 + (lane >> 3);
+      goff8 = (uint32_t)(row * 128 + (((lane & 7) ^ swz<8>(row)) * 16));
       gstep8 = 4096;
     } else {
       const int q0 = gw * 64 + lane;         // chunk q0: row q0 / 4, 16 keys (q0 % 4) * 16 ..
@@ -356,7 +414,9 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
         for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lv2 + (i * GT + gt) * 16) = u32x4{0, 0, 0, 0};
       }
       wait_vm<0>();
-      widen(t0, fslot(ic<0>{}), group_b ? lv0 : lk0, sc[0], 0);   // t0 + 1: in matrix phase t0
+      // V: widened (t0 + 1 in matrix phase t0); K: read as fp8, only its scale
+      if (group_b) widen(t0, fslot(ic<0>{}), lv0, sc[0], 0);
+      else if ((tid & (GT - 1)) == 0) scl[0][0] = sc[0];
     } else if (!group_b) {
       stage(t0, lk0);
       stage(min(t0 + 1, tl), lk1);
@@ -384,7 +444,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     auto iter = [&](int t, auto R) {
       constexpr int r = decltype(R)::value;
       constexpr int rp = (r + 2) % 3;
-      char* kl = kslot(ic<r>{});
+      char* kl = FP8 ? k8slot(ic<r>{}) : kslot(ic<r>{});
       char* vprev = vslot(ic<rp>{});
       // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T
       f32x16 s[2];
@@ -397,14 +457,18 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       if (!idle) {
         // opaque per-iteration copies: keep the read addresses from being
         // precomputed for all three slots outside the loop
-        uint32_t xk = kx, xv = vx, kro = krow, vro = vrow;
+        uint32_t xk = FP8 ? kx8 : kx, xv = vx, kro = FP8 ? krow8 : krow, vro = vrow;
         asm volatile("" : "+v"(xk), "+v"(xv), "+v"(kro), "+v"(vro));
         const char* kbase = kl + kro;
         const char* vbase = vprev + vro;
-        constexpr int NK = 2 * KK;
+        constexpr int NK = FP8 ? 8 : 2 * KK;   // fp8: (mb, kk, 16-byte part)
         constexpr int NR = NK + 4 * DB;
         auto rd = [&](int j) -> bf16x8 {
           if (j < NK) {
+            if constexpr (FP8) {
+              const int mb = j >> 2, kk = (j >> 1) & 1, part = j & 1;
+              return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)((4 * kk + part) * 16)) ^ xk) + mb * 32 * 128));
+            }
             const int kk = j >> 1, mb = j & 1;
             return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)(32 * kk)) ^ xk) + mb * 32 * D * 2));
           }
@@ -418,8 +482,20 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
           if (j < NK) {
-            const int kk = j >> 1, mb = j & 1;
-            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[kk], kk == 0 ? f32x16{} : s[mb], 0, 0, 0);
+            if constexpr (FP8) {
+              if (j & 1) {                   // both halves of the (mb, kk) fragment read
+                const int mb = j >> 2, kk = (j >> 1) & 1;
+                const i32x8 af = __builtin_bit_cast(
+                    i32x8, __builtin_shufflevector(__builtin_bit_cast(u32x4, fr[j - 1]), __builtin_bit_cast(u32x4, fr[j]),
+                                                   0, 1, 2, 3, 4, 5, 6, 7));
+                s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qh[kk], kk == 0 ? f32x16{} : s[mb],
+                                                                         0, 0, 0, 127, 0, 127);
+                s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, ql[kk], s[mb], 0, 0, 0, 127, 0, 127);
+              }
+            } else {
+              const int kk = j >> 1, mb = j & 1;
+              s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[kk], kk == 0 ? f32x16{} : s[mb], 0, 0, 0);
+            }
           } else {
             const int c = (j - NK) / DB, db = (j - NK) % DB;
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
@@ -434,8 +510,8 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       // the vector group, so the work fills its wait
       if constexpr (FP8) {
         wait_vm<0>();
-        widen(min(t + 1, tl), fslot(ic<r + 1>{}), group_b ? vslot(ic<(r + 1) % 3>{}) : kslot(ic<(r + 1) % 3>{}),
-              sc[(r + 1) % 3], (r + 1) % 3);
+        if (group_b) widen(min(t + 1, tl), fslot(ic<r + 1>{}), vslot(ic<(r + 1) % 3>{}), sc[(r + 1) % 3], (r + 1) % 3);
+        else if ((tid & (GT - 1)) == 0) scl[0][(r + 1) % 3] = sc[(r + 1) % 3];
       }
       lds_barrier();
 
@@ -460,7 +536,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
         // fp8: the K scale of tile t multiplies its logits; its V scale
         // multiplies P(t) (folded into the exponent), the row sum is
         // divided by it back
-        const float sl = FP8 ? a.scale_log2 * scl[0][r] : a.scale_log2;
+        const float sl = FP8 ? a.scale_log2 * scl[0][r] * qs : a.scale_log2;
         if (t == t0) {
           float mx = -INFINITY;
 #pragma unroll

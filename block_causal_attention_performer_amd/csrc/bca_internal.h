@@ -13,6 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kKeyTile = 64;        // keys per attention tile (a tile never straddles a >=64 page)
 constexpr int kAttnFlagWaves = 8;   // overflow flags per (query tile, split) of the fast attention kernel

@@ -1,4 +1,5 @@
-"""Why attention over an fp8 cache keeps its MFMA operands Q and P in bf16.
+"""Why attention over an fp8 cache keeps P in bf16 and gives its fp8 MFMA
+for S = K Q^T the queries as two E4M3 terms.
 
 gfx950's fp8 MFMAs would need Q (for S = K Q^T) and the softmax weights P
 (for O = P V) in E4M3 as well.  Rounding either to 3 mantissa bits costs far
@@ -15,8 +16,9 @@ is the fp8 attention tests' relative RMS of 1e-2:
   not once the softmax is sharp (Q and K x4: ≈5e-2).
 * Q as a sum of two E4M3 terms (high part, then the rounded remainder) is
   as accurate as bf16 Q (1.4e-3 against 3.6e-3 for rounding the sharp case's
-  fp32 Q to bf16), but then S needs two fp8 MFMAs, as many cycles as one
-  bf16 MFMA pass, so the fp8 rate buys nothing.
+  fp32 Q to bf16).  S then takes two fp8 MFMAs, as many cycles as one bf16
+  MFMA pass, but K is read as its codes, with no widening: the attention
+  kernel over an fp8 cache does this.
 """
 import numpy as np
 import torch

@@ -96,6 +96,25 @@ def test_fp8_attention(ws, n_kv, n_q, ps):
     assert_close(np64(out), want, FP8_TOL, FP8_REL, what="fp8 attention")
 
 
+@pytest.mark.parametrize("n_kv,n_q,ps", [(3000, 200, 256), (1000, 300, 64)])
+def test_fp8_attention_sharp_softmax(n_kv, n_q, ps):
+    """Logits x4 (Q and K drawn at 2.0, logit std ~4) on the fast path, where
+    S runs on the fp8 MFMA with Q as two E4M3 terms: a single E4M3 Q term
+    would miss the relative-RMS bar several times over here."""
+    H, D = 2, 128
+    say(f"fp8 attention sharp n_kv={n_kv} n_q={n_q} ps={ps}")
+    q = workloads.qkv(61, n_q, H, D, 2.0, "bf16")
+    k = workloads.qkv(62, n_kv, H, D, 2.0, "bf16")
+    v = workloads.qkv(63, n_kv, H, D, 0.5, "bf16")
+    g, o, _ = make_caches(bca, H, D, ps, "fp8", n_kv, 4)
+    bca.kv_append(g, k.cuda(), v.cuda())
+    o.append(k.float().numpy(), v.float().numpy())
+    out = bca.block_causal_attn(q.cuda(), g, workspace=bca.alloc_workspace(bca.workspace_bytes(g, n_q, n_kv)))
+    K, V = o.gather()
+    want = oracle.attention_dense(q.double().numpy(), K, V, n_kv - n_q, n_q)
+    assert_close(np64(out), want, FP8_TOL, FP8_REL, what="fp8 attention, sharp softmax")
+
+
 def test_fp8_c4_full_size():
     """The long-history fp8 workload: 750 units of history (2,784,000 tokens,
     10,875 pages) appended chunk by chunk plus the 3712-token unit, 40 heads
