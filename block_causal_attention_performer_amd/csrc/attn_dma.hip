@@ -351,12 +351,11 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     asm volatile("" : "+v"(si));
     return (group_b ? a.v_scales : a.k_scales)[si];
   };
-  // fp8: widen the chunks this thread loaded (fp8 slot `src`) into the
-  // swizzled bf16 slot `dst` (exact: E4M3 fits bf16), zeroing V^T entries
-  // of keys >= n_kv, and publish the tile's scale in scl[group][ss].  K:
-  // chunk q = row q / 8, head dims (q % 8) * 16 .. +15 -> bf16 chunks
-  // 2 (q % 8) and + 1 of that row.  V^T: chunk q = head-dim row q / 4,
-  // keys (q % 4) * 16 .. +15 -> bf16 chunks 2 (q % 4) and + 1.
+  // fp8, group B: widen the V^T chunks this thread loaded (fp8 slot `src`)
+  // into the swizzled bf16 slot `dst` (exact: E4M3 fits bf16), zeroing the
+  // entries of keys >= n_kv, and publish the tile's scale in scl[1][ss].
+  // Chunk q = head-dim row q / 4, keys (q % 4) * 16 .. +15 -> bf16 chunks
+  // 2 (q % 4) and + 1 of that row.
   auto widen = [&](int t, const char* src, char* dst, float sc, int ss) {
     const int gt = tid & (GT - 1);
     const int64_t k0 = (int64_t)t * BN;
@@ -373,29 +372,22 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
         hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w + 2], 1.0f, false));
         hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w + 2], 1.0f, true));
       }
-      if (!group_b) {
-        const int row = q >> 3, c16 = q & 7;
-        char* rp = dst + row * 256;
-        *reinterpret_cast<u32x4*>(rp + (((2 * c16) ^ swz<16>(row)) * 16)) = lo;
-        *reinterpret_cast<u32x4*>(rp + (((2 * c16 + 1) ^ swz<16>(row)) * 16)) = hi;
-      } else {
-        const int d = q >> 2, c = q & 3;
-        if (nvalid < BN) {
+      const int d = q >> 2, cq = q & 3;
+      if (nvalid < BN) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int key = 16 * c + 2 * w;
-            if (key >= nvalid) lo[w] &= 0xFFFF0000u;
-            if (key + 1 >= nvalid) lo[w] &= 0x0000FFFFu;
-            if (key + 8 >= nvalid) hi[w] &= 0xFFFF0000u;
-            if (key + 9 >= nvalid) hi[w] &= 0x0000FFFFu;
-          }
+        for (int w = 0; w < 4; ++w) {
+          const int key = 16 * cq + 2 * w;
+          if (key >= nvalid) lo[w] &= 0xFFFF0000u;
+          if (key + 1 >= nvalid) lo[w] &= 0x0000FFFFu;
+          if (key + 8 >= nvalid) hi[w] &= 0xFFFF0000u;
+          if (key + 9 >= nvalid) hi[w] &= 0x0000FFFFu;
         }
-        char* rp = dst + d * 128;
-        *reinterpret_cast<u32x4*>(rp + (((2 * c) ^ swz<8>(d)) * 16)) = lo;
-        *reinterpret_cast<u32x4*>(rp + (((2 * c + 1) ^ swz<8>(d)) * 16)) = hi;
       }
+      char* rp = dst + d * 128;
+      *reinterpret_cast<u32x4*>(rp + (((2 * cq) ^ swz<8>(d)) * 16)) = lo;
+      *reinterpret_cast<u32x4*>(rp + (((2 * cq + 1) ^ swz<8>(d)) * 16)) = hi;
     }
-    if (gt == 0) scl[group_b ? 1 : 0][ss] = sc;
+    if (gt == 0) scl[1][ss] = sc;
   };
 
   // ------------------------------------------------------------ main loop
