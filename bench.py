@@ -357,7 +357,9 @@ def main():
         bca.fm_euler_step(z, osc, inp["w"], 1.0 / S, workspace=ws)
         hip.record(e1, stream)
         eul_ms.append(hip.elapsed_ms(e0, e1))
-    app_bytes = 2 * 2 * lq * H * D * 2            # read + write, K and V
+    # K and V read as bf16, written as bf16 (or fp8 codes; the per-page
+    # scales are negligible)
+    app_bytes = 2 * lq * H * D * (2 + (1 if w.dtype == "fp8" else 2))
     eul_bytes = lq * H * D * 2 + H * D * 16 * 4 + 2 * lq * 16 * 4
     app_med = sorted(app_ms)[len(app_ms) // 2]
     eul_med = sorted(eul_ms)[len(eul_ms) // 2]
@@ -398,7 +400,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 S (Q as two e4m3 terms), bf16 PV" if w.dtype == "fp8" else "bf16",
         "data": "synthetic (seeded device draws, 0.5*N(0,1) Q/K/V rounded to bf16)",
         "config": {"workload": w.name, "heads": H, "head_dim": D, "unit_tokens": lq,
                    "hist_tokens": w.n_hist, "n_kv": w.n_kv, "page_size": ps,
@@ -413,7 +415,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic() if w.name == METRIC_WORKLOAD else None,
-                     "kernel": ATTN_KERNEL_NAME,
+                     "kernel": "attn_dma_kernel<128, true>" if w.dtype == "fp8" else ATTN_KERNEL_NAME,
                      "avg_launch_ms": round(attn_avg, 4), "flops_per_launch": flops_call},
         "kernels": {
             "kv_append": {"median_ms": round(app_med, 5), "bytes": app_bytes,
