@@ -97,24 +97,18 @@ __global__ void append_edge_kernel(AppendArgs a, int64_t g0, int64_t g1) {
 
 // ------------------------------------------------------------------ fp8
 
-// Round-to-nearest-even onto the finite OCP E4M3FN values, saturating at
-// 448 (OCP 8-bit floating point spec: bias 7, 3 mantissa bits, subnormal
-// quantum 2^-9, S.1111.111 reserved for NaN).  Sign copied from x.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), 448.0f);
-  if (a < 0x1p-6f) {
-    // subnormal range: code = round-half-even(a / 2^-9); a * 512 is exact
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  const uint32_t b = __float_as_uint(a);
-  const uint32_t m = b & 0x7FFFFFu;
-  uint32_t keep = m >> 20;
-  const uint32_t rem = m & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
-  uint32_t e = (b >> 23) - 127 + 7;
-  if (keep == 8) { keep = 0; ++e; }
-  return sign | (e << 3) | keep;
+// Round-to-nearest-even onto the finite OCP E4M3FN values (OCP 8-bit
+// floating point spec: bias 7, 3 mantissa bits, subnormal quantum 2^-9,
+// S.1111.111 reserved for NaN), saturating at 448, two values at once by the
+// hardware conversion (v_cvt_pk_fp8_f32) into bytes 0-1 (HI = false) or 2-3
+// (HI = true) of `old`.  The inputs are clamped to +-448 first (the
+// saturation).  The append tests check the codes bit for bit against the
+// oracle's encoder (ties, subnormals, saturation).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_rne_sat(float x, float y, uint32_t old) {
+  x = fminf(fmaxf(x, -448.0f), 448.0f);
+  y = fminf(fmaxf(y, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, y, (int)old, HI);
 }
 
 __device__ __forceinline__ float block_max_256(float v, float* red) {
@@ -171,25 +165,22 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(AppendArgs a) {
     // codes: 8 values (one 16-byte bf16 vector) per thread per pass
     for (int i = threadIdx.x; i < ps * (D / 8); i += kThreads) {
       const int r = i / (D / 8), c = i % (D / 8);
-      uint32_t code[8];
+      uint32_t dw[2] = {0u, 0u};             // codes 0..3, 4..7 (byte e of dw[e / 4])
       if (r < r1) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + ((t0 - a.n0 + r) * H + h) * D + c * 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          code[2 * e] = e4m3_rne_sat(__uint_as_float(v[e] << 16) * inv);
-          code[2 * e + 1] = e4m3_rne_sat(__uint_as_float(v[e] & 0xFFFF0000u) * inv);
+        for (int e = 0; e < 4; e += 2) {
+          dw[e >> 1] = e4m3x2_rne_sat<false>(__uint_as_float(v[e] << 16) * inv,
+                                             __uint_as_float(v[e] & 0xFFFF0000u) * inv, 0u);
+          dw[e >> 1] = e4m3x2_rne_sat<true>(__uint_as_float(v[e + 1] << 16) * inv,
+                                            __uint_as_float(v[e + 1] & 0xFFFF0000u) * inv, dw[e >> 1]);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) code[e] = 0;
       }
       if (which == 0) {
-        uint32_t lo = code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
-        uint32_t hi = code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24;
-        *reinterpret_cast<uint2*>(kp + (int64_t)r * D + c * 8) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(kp + (int64_t)r * D + c * 8) = make_uint2(dw[0], dw[1]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vt[(c * 8 + e) * (ps + 4) + r] = (uint8_t)code[e];
+        for (int e = 0; e < 8; ++e) vt[(c * 8 + e) * (ps + 4) + r] = (uint8_t)(dw[e >> 2] >> (8 * (e & 3)));
       }
     }
     if (which == 1) {
