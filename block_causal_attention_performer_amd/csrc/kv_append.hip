@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(AppendArgs a) {
     for (int i = threadIdx.x; i < ps * (D / 8); i += kThreads) {
       const int r = i / (D / 8), c = i % (D / 8);
       uint32_t dw[2] = {0u, 0u};             // codes 0..3, 4..7 (byte e of dw[e / 4])
-      if (r < r1) {
+      if (r < r1 && amax != 0.0f) {           // an all-zero block (-0 too) gets codes 0
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + ((t0 - a.n0 + r) * H + h) * D + c * 8);
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {

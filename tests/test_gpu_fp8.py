@@ -64,6 +64,23 @@ def test_fp8_append_bit_exact(ps, shuffle):
     _bits_equal(g, o, sum(sizes), ps)
 
 
+def test_fp8_append_zero_blocks():
+    """A (page, head) block of zeros, negative zeros among them, gets scale 1
+    and codes 0, as the oracle's quantiser defines for amax = 0; a block of
+    only -0 beside a normal one in the same page."""
+    H, D, ps = 2, 128, 64
+    x = torch.zeros((ps, H, D), dtype=torch.bfloat16)
+    x[::3, 0] = -0.0                           # head 0: zeros and negative zeros
+    x[:, 1] = workloads.qkv(71, ps, 1, D, 0.5, "bf16")[:, 0]
+    y = torch.full((ps, H, D), -0.0, dtype=torch.bfloat16)
+    g, o, _ = make_caches(bca, H, D, ps, "fp8", ps, None)
+    bca.kv_append(g, x.cuda(), y.cuda())
+    o.append(x.float().numpy(), y.float().numpy())
+    torch.cuda.synchronize()
+    _bits_equal(g, o, ps, ps)
+    assert g.k_scales[0, 0].item() == 1.0 and g.v_scales[0, 0].item() == 1.0
+
+
 def test_fp8_append_rejects_unaligned_start():
     """An fp8 append must start on a page boundary (no requantisation of a
     partly filled page): the call fails and the cache is unchanged."""
