@@ -88,11 +88,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_exact_kernel(AttnArgs a) {
   const int h = rest / a.nsplit;
   if (a.flags) {
     // rerun only the query tiles the fast kernel flagged (its tiles have the
-    // same rows: 256 per workgroup)
+    // same rows: 256 per workgroup); at most kMaxAttnSplit x kAttnFlagWaves
+    // = 64 flags, one per lane, so every wave reaches the same verdict
+    static_assert(kMaxAttnSplit * kAttnFlagWaves <= 64, "one flag per lane");
     const int32_t* f = a.flags + (int64_t)(h * nqt + qt) * a.flag_splits * kAttnFlagWaves;
-    int any = 0;
-    for (int i = 0; i < a.flag_splits * kAttnFlagWaves; ++i) any |= f[i];
-    if (!any) return;
+    const int fl = lane < a.flag_splits * kAttnFlagWaves ? f[lane] : 0;
+    if (__builtin_amdgcn_ballot_w64(fl != 0) == 0) return;
   }
 
   const int64_t B = a.block_size;
