@@ -317,11 +317,16 @@ def performer_unit(cache, k_new, v_new, q, w, eps, n_steps: int,
     whole cache, projected by W.  Q/K/V do not change across solver steps,
     so the attention output is computed once.  Returns (z(0), O).  With rows
     given, only those query rows are evaluated (all heads are needed for the
-    projection)."""
+    projection).
+
+    The unit is one block [explainer, figure caption: the tokens of a block
+    see each other in both directions and every earlier block]: its slice is
+    the last append, so each of its queries sees every cached key, its own
+    slice included, whatever the history length.  (A fixed grid t // n_q
+    would cut the unit in two when the history is not a multiple of n_q.)"""
     cache.append(k_new, v_new)
     K, V = cache.gather()
-    n_q = np.asarray(q).shape[0]
-    o = attention_dense(q, K, V, cache.n_tokens - n_q, n_q, scale, rows=rows)
+    o = attention_dense(q, K, V, scale=scale, rows=rows)
     v = velocity(o, w)
     eps = np.asarray(eps, dtype=np.float64)
     if rows is not None:

@@ -347,3 +347,30 @@ def test_performer_unit_composes_pieces():
     want_o = _sdpa(q, K, V)
     np.testing.assert_allclose(o, want_o, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(z, eps - (want_o.reshape(B, -1) @ w), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_hist,B", [(12, 5), (7, 4), (0, 3), (30, 7)])
+def test_performer_unit_sees_its_whole_slice_on_any_history(n_hist, B):
+    """The unit is one block whose tokens see each other both ways (explainer,
+    figure caption of the block-causal mask), also when the history is not a
+    multiple of the unit: with a 12-token history and a 5-token unit, query 0
+    (global position 12) must see key 16, the unit's last.  A key planted
+    there as a large multiple of query 0 takes all of that query's weight,
+    so its output is that key's value; and every row equals unmasked
+    attention over the whole cache (torch float64)."""
+    H, D, ps = 2, 8, 4
+    n_pages = -(-(n_hist + B) // ps)
+    pt = list(np.random.default_rng(n_hist).permutation(n_pages))
+    c = oracle.PagedCache(H, D, ps, pt, n_pages)
+    hist_k, hist_v = _rand(n_hist, H, D), _rand(n_hist, H, D)
+    if n_hist:
+        c.append(hist_k, hist_v)
+    kn, vn, q = _rand(B, H, D), _rand(B, H, D), _rand(B, H, D)
+    # the unit's last key, matched to query 0: logit 200/sqrt(D) ~ 70 per head
+    kn[B - 1] = q[0] * (200.0 / np.sum(q[0] * q[0], axis=-1, keepdims=True))
+    w = _rand(H * D, 3)
+    z, o = oracle.performer_unit(c, kn, vn, q, w, _rand(B, 3), 4)
+    np.testing.assert_allclose(o[0], vn[B - 1], rtol=0, atol=1e-9)
+    K = np.concatenate([hist_k, kn])
+    V = np.concatenate([hist_v, vn])
+    np.testing.assert_allclose(o, _sdpa(q, K, V), rtol=1e-12, atol=1e-13)
