@@ -31,11 +31,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def sources():
+    """The library's HIP sources (every *.hip under csrc/)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
 def build(defines=(), out: str = LIB, verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sources()
     tag = "_".join(d.replace("=", "") for d in defines) or "default"
     objdir = os.path.join(HERE, "_build", tag)
     os.makedirs(objdir, exist_ok=True)
+    # drop objects whose source is gone, so nothing links a deleted kernel
+    keep = {os.path.basename(src) + ".o" for src in srcs}
+    for o in glob.glob(os.path.join(objdir, "*.hip.o")):
+        if os.path.basename(o) not in keep:
+            os.remove(o)
     dflags = [f"-D{d}" for d in defines]
     cc = hipcc()
 

@@ -421,9 +421,10 @@ bca_status check_performer(const bca_kv_cache* c, const void* k_new, const void*
   bca_status st = check_append(c, k_new, v_new, n_q, io);
   if (st != BCA_OK) return st;
   const int64_t n_kv = c->n_tokens + n_q;
+  if (n_kv > INT32_MAX) return BCA_EINVAL;    // the unit's block size is n_kv (int32)
   bca_kv_cache after = *c;
   after.n_tokens = n_kv;
-  st = check_attn(q, n_q, n_kv - n_q, (int32_t)n_q, &after, n_kv, o_scratch, io, io, 0.0f);
+  st = check_attn(q, n_q, n_kv - n_q, (int32_t)n_kv, &after, n_kv, o_scratch, io, io, 0.0f);
   if (st != BCA_OK) return st;
   const int32_t kdim = c->n_heads * c->head_dim;
   st = check_euler(z, o_scratch, w, n_q, kdim, n_ch, 1.0f / (float)n_steps, io);
@@ -451,7 +452,9 @@ bca_status enqueue_performer(bca_kv_cache* c, const void* k_new, const void* v_n
   for (int32_t step = 0; step < n_steps; ++step) {
     hipEvent_t* ev = attn_events ? attn_events + 3 * step : nullptr;
     if (ev && hipEventRecord(ev[0], s) != hipSuccess) return BCA_EHIP;
-    st = enqueue_attn(q, n_q, n_kv - n_q, (int32_t)n_q, c, n_kv, o_scratch, io, 0.0f, attn_ws,
+    // the unit is one block: its queries see every cached key, their own
+    // slice included, whatever the history length (block size n_kv)
+    st = enqueue_attn(q, n_q, n_kv - n_q, (int32_t)n_kv, c, n_kv, o_scratch, io, 0.0f, attn_ws,
                       attn_room, ev ? ev[1] : nullptr, s);
     if (st != BCA_OK) return st;
     if (ev && hipEventRecord(ev[2], s) != hipSuccess) return BCA_EHIP;
@@ -477,12 +480,19 @@ __global__ void pt_set_kernel(int32_t* pt, PtUpdate u) {
 
 }  // namespace
 
+// Graph units alternate between two instantiated graphs.  A graph is
+// updated (or destroyed) only once its previous launch, two units back, has
+// finished (its event): rewriting the kernel arguments of an instantiated
+// graph whose launch may still be queued on the stream is not something
+// the runtime promises to keep from that launch.
 struct bca_session {
   bca_kv_cache* cache;
   std::vector<int32_t> free_pages;   // handed out in this order
   size_t next_free;
   int64_t mapped;                    // logical pages [0, mapped) have physical pages
-  hipGraphExec_t exec;               // last instantiated unit graph (updated in place)
+  hipGraphExec_t exec[2];            // unit graphs, used in turn (updated in place)
+  hipEvent_t done[2];                // recorded on the stream after each one's launch
+  int next_exec;                     // slot of the next graph unit
   hipStream_t cap;                   // capture-only stream (nothing executes on it)
 };
 
@@ -568,7 +578,9 @@ bca_status bca_session_create(bca_kv_cache* c, const int32_t* free_pages, int32_
   ss->free_pages.assign(free_pages, free_pages + n_free);
   ss->next_free = 0;
   ss->mapped = (c->n_tokens + c->page_size - 1) / c->page_size;
-  ss->exec = nullptr;
+  ss->exec[0] = ss->exec[1] = nullptr;
+  ss->done[0] = ss->done[1] = nullptr;
+  ss->next_exec = 0;
   ss->cap = nullptr;
   *out = ss;
   return BCA_OK;
@@ -614,24 +626,36 @@ bca_status bca_session_unit(bca_session* ss, const void* k_new, const void* v_ne
   if (graph) {
     const hipError_t ec = hipStreamEndCapture(ls, &g);
     if (st == BCA_OK && ec != hipSuccess) st = BCA_EHIP;
+    const int slot = ss->next_exec;
+    hipGraphExec_t& ex = ss->exec[slot];
+    if (st == BCA_OK && !ss->done[slot] &&
+        hipEventCreateWithFlags(&ss->done[slot], hipEventDisableTiming) != hipSuccess) {
+      ss->done[slot] = nullptr;
+      st = BCA_EHIP;
+    }
+    // this slot's previous launch (two units back) must be over before its
+    // graph is rewritten
+    if (st == BCA_OK && ex && hipEventSynchronize(ss->done[slot]) != hipSuccess) st = BCA_EHIP;
     if (st == BCA_OK) {
-      if (ss->exec) {
+      if (ex) {
         hipGraphNode_t bad = nullptr;
         hipGraphExecUpdateResult res;
-        if (hipGraphExecUpdate(ss->exec, g, &bad, &res) != hipSuccess || res != hipGraphExecUpdateSuccess) {
+        if (hipGraphExecUpdate(ex, g, &bad, &res) != hipSuccess || res != hipGraphExecUpdateSuccess) {
           // a different shape (new page entries or not, another split
           // count): instantiate afresh, and clear the refused update from
           // the thread's last-error state
           (void)hipGetLastError();
-          (void)hipGraphExecDestroy(ss->exec);
-          ss->exec = nullptr;
+          (void)hipGraphExecDestroy(ex);
+          ex = nullptr;
         }
       }
-      if (!ss->exec && hipGraphInstantiate(&ss->exec, g, nullptr, nullptr, 0) != hipSuccess) {
-        ss->exec = nullptr;
+      if (!ex && hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) != hipSuccess) {
+        ex = nullptr;
         st = BCA_EHIP;
       }
-      if (st == BCA_OK && hipGraphLaunch(ss->exec, s) != hipSuccess) st = BCA_EHIP;
+      if (st == BCA_OK && hipGraphLaunch(ex, s) != hipSuccess) st = BCA_EHIP;
+      if (st == BCA_OK && hipEventRecord(ss->done[slot], s) != hipSuccess) st = BCA_EHIP;
+      if (st == BCA_OK) ss->next_exec = slot ^ 1;
     }
     if (g) (void)hipGraphDestroy(g);
   }
@@ -650,7 +674,11 @@ int64_t bca_session_free_pages(const bca_session* ss) {
 
 void bca_session_destroy(bca_session* ss) {
   if (!ss) return;
-  if (ss->exec) (void)hipGraphExecDestroy(ss->exec);
+  for (int i = 0; i < 2; ++i) {
+    if (ss->done[i]) (void)hipEventSynchronize(ss->done[i]);   // no launch of it still queued
+    if (ss->exec[i]) (void)hipGraphExecDestroy(ss->exec[i]);
+    if (ss->done[i]) (void)hipEventDestroy(ss->done[i]);
+  }
   if (ss->cap) (void)hipStreamDestroy(ss->cap);
   delete ss;
 }

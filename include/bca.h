@@ -27,10 +27,14 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library allocates no device buffers and keeps no global state.  The
- *     streaming session (bca_session_*) is the one object the library
- *     creates: host bookkeeping plus the HIP graph it replays, owned by
- *     the caller through the session handle.
+ *     library allocates no device buffers.  Its only state across calls is
+ *     host-side: a 16-entry memo of the attention split count per call
+ *     shape (behind a mutex, so calls from several threads are safe; it
+ *     changes no result, only which split count a shape gets without
+ *     re-running the model that picks it).  The streaming session
+ *     (bca_session_*) is the one object the library creates: host
+ *     bookkeeping plus the HIP graphs it replays, owned by the caller
+ *     through the session handle.
  *   - Work is enqueued asynchronously on the caller's stream `s`; calls
  *     return after enqueue.  Two calls that share a cache or a workspace
  *     must be ordered by the caller (same stream or events).
@@ -133,7 +137,11 @@ BCA_API bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_n
  *        with an f32 cache)
  *   q_pos0: global position of query row 0; requires 0 <= q_pos0 and
  *        q_pos0 + n_q <= n_kv <= c->n_tokens.
- *        Streaming call: q_pos0 = n_kv - n_q, block_size = n_q (all visible).
+ *        Streaming call: q_pos0 = n_kv - n_q, block_size = n_kv: every key
+ *        below n_kv is visible to every query, whatever n_kv - n_q is.
+ *        (block_size = n_q gives the same only when n_kv - n_q is a
+ *        multiple of n_q; otherwise the grid j / n_q cuts the queries'
+ *        block in two.)
  *        Full sequence:  q_pos0 = 0, n_q = n_kv.  block_size = 1 is causal.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   workspace: optional device scratch (may be NULL) of workspace_bytes.
@@ -181,11 +189,15 @@ BCA_API bca_status fm_euler_step(float* z, const void* x, const float* w,
  * performer_unit -- one streaming unit of the performer (deep read section 4
  * step 3; wiki contribution 3 table): kv_append(k_new, v_new); then for
  * s = 0 .. n_steps-1: block_causal_attn of q over the whole cache
- * (q_pos0 = n_tokens - n_q, block_size = n_q) into o_scratch, then
- * fm_euler_step(z, o_scratch, w, dtau = 1/n_steps).
+ * (n_kv = n_tokens after the append, q_pos0 = n_kv - n_q, block_size = n_kv)
+ * into o_scratch, then fm_euler_step(z, o_scratch, w, dtau = 1/n_steps).
+ * The unit is one block: its queries see every cached key, their own slice
+ * in both directions (explainer, figure caption of the block-causal mask),
+ * also when the history is not a multiple of n_q.  n_tokens + n_q must not
+ * exceed INT32_MAX (BCA_EINVAL).
  *
  *   k_new, v_new, q: [n_q][n_heads][head_dim] (f32 for an f32 cache, else
- *                    bf16); the unit is one block of n_q tokens
+ *                    bf16)
  *   w:  [n_heads*head_dim][n_ch] fp32;  z: [n_q][n_ch] fp32, noise in,
  *       clean latents out
  *   o_scratch: [n_q][n_heads][head_dim] (f32 for an f32 cache, else bf16)
@@ -219,16 +231,20 @@ BCA_API bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void
  *   free_pages (host array of n_free distinct physical page ids in
  *   [0, n_phys_pages), none of them in use) is copied.  Errors: EINVAL.
  * bca_session_unit: one performer_unit (same arguments and result) after
- *   the page mapping.  use_graph != 0: the unit's launches are captured on
- *   s into a HIP graph and replayed (the previous unit's instantiated graph
- *   is updated in place when its shape allows); on a stream that is
- *   already being captured the launches simply join that capture.  Errors
+ *   the page mapping.  use_graph != 0: the unit's launches are captured
+ *   into a HIP graph and launched on s.  Graph units alternate between two
+ *   instantiated graphs; each is updated in place when the new unit's
+ *   shape allows, but only after its previous launch (two graph units
+ *   back) has finished, which the call waits for on the host.  So one unit
+ *   may be queued ahead of the GPU without blocking the host.  On a stream
+ *   that is already being captured the launches simply join that capture.
+ *   Errors
  *   as performer_unit, plus ERANGE when free_pages cannot cover the unit;
  *   on error nothing of the unit is committed (n_tokens and the page count
  *   unchanged).
  * bca_session_free_pages: free pages left (-1 for NULL).
- * bca_session_destroy: releases the graph and the session (NULL is a no-op);
- *   the caller must have synchronised s first.
+ * bca_session_destroy: waits for the session's graph launches to finish,
+ *   then releases the graphs and the session (NULL is a no-op).
  * Calls on one session must be ordered by the caller.
  */
 typedef struct bca_session bca_session;

@@ -50,3 +50,15 @@ def make_caches(bca, H, D, ps, dtype, capacity, shuffle=None, extra=2, device="c
     else:
         o = oracle.PagedCache(H, D, ps, pt.numpy(), n_phys)
     return g, o, pt
+
+
+def assert_latents(z_got, z_want, eps, max_abs, rel_rms=1e-2, what=""):
+    """Latents after the solver: z itself within max_abs, and the solver's
+    move z - eps (= -sum of dtau * v) within relative RMS `rel_rms`.  With
+    |eps| ~ 1 and a move of ~0.1, a check of z alone at rel_rms would let a
+    velocity several percent off pass."""
+    z_got = np.asarray(z_got, dtype=np.float64)
+    z_want = np.asarray(z_want, dtype=np.float64)
+    eps = np.asarray(eps, dtype=np.float64)
+    assert_close(z_got, z_want, max_abs, what=f"{what} z")
+    assert_close(z_got - eps, z_want - eps, max_abs, rel_rms, what=f"{what} z - eps")

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_causal_attention_performer_amd as bca
 
@@ -184,3 +185,47 @@ def test_session_unit_validates_before_mapping():
                                   None) == -1
     finally:
         L.bca_session_destroy(h)
+
+
+# ------------------------------------------------- binding argument checks
+
+
+def test_binding_rejects_host_cache():
+    """The kernels take raw device pointers: a cache on the host is refused
+    before anything is allocated or launched."""
+    pt = torch.arange(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="not a CUDA"):
+        bca.KVCache(2, 128, 256, pt, 4, "bf16", device="cpu")
+
+
+@pytest.mark.parametrize("pt,n_phys,msg", [
+    ([0, 1, 1], 4, "twice"),
+    ([0, 4], 4, "outside"),
+    ([-2, 0], 4, "outside"),
+    ([], 4, "empty"),
+])
+def test_binding_checks_page_table(pt, n_phys, msg):
+    with pytest.raises(ValueError, match=msg):
+        bca.check_page_table(torch.tensor(pt, dtype=torch.int32), n_phys)
+
+
+def test_binding_page_table_allows_unmapped():
+    assert bca.check_page_table(torch.tensor([3, -1, 0, -1]), 4) == [3, -1, 0, -1]
+
+
+def test_binding_tensor_checks():
+    dev = torch.device("cpu")
+    t = torch.zeros((4, 2, 8), dtype=torch.bfloat16)
+    bca._need(t, "t", dev, (torch.bfloat16,), (4, 2, 8))
+    with pytest.raises(ValueError, match="dtype"):
+        bca._need(t.float(), "t", dev, (torch.bfloat16,), (4, 2, 8))
+    with pytest.raises(ValueError, match="shape"):
+        bca._need(t[:3], "t", dev, (torch.bfloat16,), (4, 2, 8))
+    with pytest.raises(ValueError, match="contiguous"):
+        bca._need(t.transpose(0, 1), "t", dev, (torch.bfloat16,))
+    with pytest.raises(ValueError, match="elements"):
+        bca._need(t, "t", dev, (torch.bfloat16,), numel=63)
+    with pytest.raises(ValueError, match="on meta"):
+        bca._need(torch.empty(4, device="meta"), "t", dev, (torch.float32,))
+    with pytest.raises(ValueError, match="required"):
+        bca._need(None, "t", dev, (torch.float32,))

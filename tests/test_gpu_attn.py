@@ -76,16 +76,35 @@ def _bf16_case(H, D, n_kv, ps, shuffle, seed, scale=1.0):
 @pytest.mark.parametrize("n_kv,n_q", [(1000, 300), (4160, 777), (300, 300), (70, 5)])
 @pytest.mark.parametrize("ws", [False, True])
 def test_bf16_streaming(D, ps, shuffle, n_kv, n_q, ws):
-    """The streaming call: the last n_q tokens form the current block and see
-    every cached key; ragged key and query tails."""
+    """The streaming call (the binding's defaults: q_pos0 = n_kv - n_q,
+    block_size = n_kv): the last n_q tokens form the current block and see
+    every cached key, also where the history (700, 3383, 65) is not a
+    multiple of n_q; ragged key and query tails."""
     H = 3
     say(f"bf16 streaming D={D} ps={ps} n_kv={n_kv} n_q={n_q} ws={ws}")
     q, k, v, g, _ = _bf16_case(H, D, n_kv, ps, shuffle, 31)
     qq = q[n_kv - n_q:]
     out = bca.block_causal_attn(qq.cuda(), g, workspace=_ws(g, n_q, n_kv, ws))
-    want = oracle.attention_dense(qq.double().numpy(), k.double().numpy(), v.double().numpy(),
-                                  n_kv - n_q, n_q)
+    want = oracle.attention_dense(qq.double().numpy(), k.double().numpy(), v.double().numpy())
     assert_close(np64(out), want, BF16_TOL, BF16_REL, what="streaming bf16")
+
+
+@pytest.mark.parametrize("ws", [False, True])
+@pytest.mark.parametrize("n_kv,n_q,B", [(1000, 300, 300), (4160, 777, 777), (2000, 600, 256)])
+def test_bf16_explicit_grid_cuts_the_queries(n_kv, n_q, B, ws):
+    """An explicit block grid that does not line up with the queries: q_pos0
+    = n_kv - n_q with block_size B puts the queries in two or more blocks
+    of the fixed grid j // B, so their early rows must not see the later
+    keys of the call.  The oracle's dense mask with the same grid decides."""
+    H, D = 2, 128
+    say(f"bf16 explicit grid n_kv={n_kv} n_q={n_q} B={B} ws={ws}")
+    q, k, v, g, _ = _bf16_case(H, D, n_kv, 64, 5, 37)
+    qq = q[n_kv - n_q:]
+    out = bca.block_causal_attn(qq.cuda(), g, q_pos0=n_kv - n_q, block_size=B,
+                                workspace=_ws(g, n_q, n_kv, ws))
+    want = oracle.attention_dense(qq.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                  n_kv - n_q, B)
+    assert_close(np64(out), want, BF16_TOL, BF16_REL, what=f"grid B={B}")
 
 
 @pytest.mark.parametrize("B", [1, 16, 100, 256, 1000])
@@ -130,8 +149,10 @@ def test_split_kv_matches_single_pass():
     b = bca.block_causal_attn(qq, g, workspace=ws)
     c = bca.block_causal_attn(qq, g, workspace=ws)
     torch.cuda.synchronize()
+    # the streaming call: every one of the n_kv keys visible (the history,
+    # 19,744 tokens, is not a multiple of the 256 queries)
     want = oracle.attention_dense(q[n_kv - n_q:].double().numpy(), k.double().numpy(),
-                                  v.double().numpy(), n_kv - n_q, n_q)
+                                  v.double().numpy())
     assert_close(np64(a), want, BF16_TOL, BF16_REL, what="single pass")
     assert_close(np64(b), want, BF16_TOL, BF16_REL, what="split")
     assert torch.equal(b, c)
@@ -159,7 +180,7 @@ def test_every_split_count():
     q, k, v, g, _ = _bf16_case(H, D, n_kv, 256, 2, 93)
     qq = q[n_kv - n_q:].cuda()
     want = oracle.attention_dense(q[n_kv - n_q:].double().numpy(), k.double().numpy(),
-                                  v.double().numpy(), n_kv - n_q, n_q)
+                                  v.double().numpy())
     outs = []
     for s in range(1, 9):
         ws = bca.alloc_workspace(_split_ws_bytes(n_q, H, D, s))
@@ -214,5 +235,5 @@ def test_peaky_planted_keys(ws):
     scale = 4.0 / np.sqrt(D)
     out = bca.block_causal_attn(q.cuda(), g, softmax_scale=scale, workspace=_ws(g, n_q, n_kv, ws))
     want = oracle.attention_dense(q.double().numpy(), k.double().numpy(), v.double().numpy(),
-                                  n_kv - n_q, n_q, scale=scale)
+                                  scale=scale)
     assert_close(np64(out), want, BF16_TOL, BF16_REL, what="peaky")
