@@ -7,6 +7,9 @@ and shares no code, header, table or helper with it.
 Every function is the plain definition of what the performer step computes,
 in float64 (float32 where the method fixes a float32 decision, e.g. the fp8
 quantiser's product).  See ``oracle/performer.py`` for the citations.
+``oracle/fp8c.py`` (with ``oracle/fp8_cache.c``) is the fp8 quantiser and
+decoder once more in plain C, fast enough for the long fp8 history; it is
+pinned bit for bit to ``performer.py``'s and to torch's float8 cast.
 """
 from .performer import (  # noqa: F401
     visibility_mask,
