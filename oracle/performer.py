@@ -26,7 +26,8 @@ Readings where the pages are silent (each also listed in the design notes):
     V pages [P][H][D][ps] (d-major), logical token t at physical page
     page_table[t // ps], slot t % ps;
   * fp8 storage: OCP E4M3FN codes with one fp32 scale per (page, head, K|V),
-    scale = amax/448, code = RNE-saturate(x * (448/amax)) in fp32.
+    scale = amax/448, code = RNE-saturate(x * (448/amax)) in fp32; an append
+    that starts inside a page re-quantises that page from its stored values.
 
 Pins (tests/test_oracle_pins.py): brute-force two-key closed form, torch's
 scaled_dot_product_attention in float64, dense-mask vs incremental paged
@@ -226,9 +227,16 @@ def quantize_rows(x_rows) -> tuple:
 
 class PagedCacheFP8:
     """fp8 pages: codes in the same layouts as PagedCache, one fp32 scale per
-    (physical page, head) for K and for V.  Appends must start at a page
-    boundary (a partially filled page is never requantised); rows past the
-    valid length of a page hold code 0 and do not enter amax."""
+    (physical page, head) for K and for V; rows past the valid length of a
+    page hold code 0 and do not enter amax.
+
+    An append that starts inside a partly filled page re-quantises that
+    page: the cache holds only codes, so the values of its rows already
+    stored are their dequantised values, fp32(decode(code) * scale), and the
+    page's block becomes those rows followed by the new ones, quantised by
+    the same rule as a fresh page (amax over all its valid rows).  (One scale
+    per page and head leaves no other plain choice: keeping the old scale
+    would saturate new rows larger than the old ones.)"""
 
     def __init__(self, n_heads, head_dim, page_size, page_table, n_phys):
         self.H, self.D, self.ps = n_heads, head_dim, page_size
@@ -239,25 +247,35 @@ class PagedCacheFP8:
         self.v_scales = np.ones((n_phys, n_heads), np.float32)
         self.n_tokens = 0
 
+    def stored_rows(self, page: int, h: int, n_rows: int):
+        """The values the cache holds for the first n_rows rows of (page, h):
+        fp32(decode(code) * scale), K and V, each [n_rows, D] float32."""
+        k = (e4m3_decode(self.k_codes[page, h, :n_rows, :]) * np.float64(self.k_scales[page, h]))
+        v = (e4m3_decode(self.v_codes[page, h, :, :n_rows].T) * np.float64(self.v_scales[page, h]))
+        return k.astype(np.float32), v.astype(np.float32)
+
     def append(self, k_new, v_new) -> None:
         k_new = np.asarray(k_new, dtype=np.float32)
         v_new = np.asarray(v_new, dtype=np.float32)
         n0, n = self.n_tokens, k_new.shape[0]
-        if n0 % self.ps != 0:
-            raise ValueError("fp8 append must start at a page boundary")
         if n0 + n > len(self.pt) * self.ps:
             raise ValueError("append past the mapped pages")
         for lp in range(n0 // self.ps, -(-(n0 + n) // self.ps)):
             t0 = lp * self.ps
-            r0, r1 = t0 - n0, min(n, t0 + self.ps - n0)
+            r0, r1 = max(t0 - n0, 0), min(n, t0 + self.ps - n0)
+            n_old = max(n0 - t0, 0)           # rows already in this page
             page = self.pt[lp]
             for h in range(self.H):
-                kc, ks = quantize_rows(k_new[r0:r1, h, :])
-                vc, vs = quantize_rows(v_new[r0:r1, h, :])
+                kb, vb = k_new[r0:r1, h, :], v_new[r0:r1, h, :]
+                if n_old:
+                    ko, vo = self.stored_rows(page, h, n_old)
+                    kb, vb = np.concatenate([ko, kb]), np.concatenate([vo, vb])
+                kc, ks = quantize_rows(kb)
+                vc, vs = quantize_rows(vb)
                 self.k_codes[page, h] = 0
                 self.v_codes[page, h] = 0
-                self.k_codes[page, h, :r1 - r0, :] = kc
-                self.v_codes[page, h, :, :r1 - r0] = vc.T
+                self.k_codes[page, h, :len(kb), :] = kc
+                self.v_codes[page, h, :, :len(vb)] = vc.T
                 self.k_scales[page, h] = ks
                 self.v_scales[page, h] = vs
         self.n_tokens = n0 + n

@@ -254,8 +254,11 @@ def test_fp8_cache_rows_past_valid_are_zero():
     c = oracle.PagedCacheFP8(H, D, ps, [3, 1, 0], 4)
     c.append(_rand(20, H, D), _rand(20, H, D))
     assert not c.k_codes[1, :, 4:, :].any() and not c.v_codes[1, :, :, 4:].any()
-    with pytest.raises(ValueError):
-        c.append(_rand(4, H, D), _rand(4, H, D))
+    # a mid-page append re-quantises page 1: its valid rows grow to 8 and the
+    # rows past them stay code 0
+    c.append(_rand(4, H, D), _rand(4, H, D))
+    assert c.k_codes[1, :, :8, :].any() and not c.k_codes[1, :, 8:, :].any()
+    assert not c.v_codes[1, :, :, 8:].any()
 
 
 def test_fp8_cache_gather_is_identity_on_the_grid():
@@ -374,3 +377,73 @@ def test_performer_unit_sees_its_whole_slice_on_any_history(n_hist, B):
     K = np.concatenate([hist_k, kn])
     V = np.concatenate([hist_v, vn])
     np.testing.assert_allclose(o, _sdpa(q, K, V), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------- fp8 appends inside a page
+
+
+def _e4m3_half_step(y):
+    """Half the spacing of the E4M3 grid around |y| <= 448 (in the units of
+    y): 2^-10 in the subnormal range, else 2^(e-4) for y in [2^e, 2^(e+1))."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.where(a < 2.0 ** -6, 2.0 ** -10, 2.0 ** (e - 4))
+
+
+def test_fp8_requant_keeps_values_already_on_the_grid():
+    """A page whose first rows have amax 448 * 2^-3 (scale 2^-3, exact) and lie
+    on that scale's E4M3 grid, then a mid-page append of smaller rows on the
+    same grid: the scale cannot change, so re-quantising changes nothing and
+    the split append equals one append of all rows, bit for bit."""
+    H, D, ps = 2, 16, 64
+    rng = np.random.default_rng(5)
+    grid = oracle.e4m3_decode(np.arange(0x7F)) * 2.0 ** -3          # non-negative grid values
+    x = rng.choice(grid[:100], size=(40, H, D)) * rng.choice([-1.0, 1.0], size=(40, H, D))
+    x[0] = 448.0 * 2.0 ** -3                                       # the amax, in the old rows
+    y = rng.choice(grid[:100], size=(40, H, D))
+    y[5] = 448.0 * 2.0 ** -3
+    split = oracle.PagedCacheFP8(H, D, ps, [1, 0], 2)
+    split.append(x[:23].astype(np.float32), y[:23].astype(np.float32))
+    split.append(x[23:].astype(np.float32), y[23:].astype(np.float32))
+    whole = oracle.PagedCacheFP8(H, D, ps, [1, 0], 2)
+    whole.append(x.astype(np.float32), y.astype(np.float32))
+    np.testing.assert_array_equal(split.k_codes, whole.k_codes)
+    np.testing.assert_array_equal(split.v_codes, whole.v_codes)
+    np.testing.assert_array_equal(split.k_scales, whole.k_scales)
+    K, V = split.gather()
+    np.testing.assert_array_equal(K, x)                              # exact: on the grid
+    np.testing.assert_array_equal(V, y)
+
+
+@pytest.mark.parametrize("n_old,grow", [(37, 4.0), (1, 0.25), (63, 1.0)])
+def test_fp8_requant_rounding_bounds(n_old, grow):
+    """Random rows, then a mid-page append whose rows are `grow` times larger:
+    every value the page now holds is one round-to-nearest of its input (the
+    old rows' input being the values they held) onto the new scale's grid,
+    within half a step; an old row also stays within half a step at the old
+    scale plus half a step at the new one of its original source; pages
+    after the split page are those of a single append, bit for bit."""
+    H, D, ps = 3, 32, 64
+    rng = np.random.default_rng(n_old)
+    n = 150
+    x = (rng.standard_normal((n, H, D)) * 0.5).astype(np.float32)
+    x[n_old:] *= np.float32(grow)
+    c = oracle.PagedCacheFP8(H, D, ps, [2, 0, 1], 3)
+    c.append(x[:n_old], x[:n_old])
+    held = c.gather()[0][:n_old]                                   # values before the append
+    s_old = c.k_scales[2].astype(np.float64)
+    c.append(x[n_old:], x[n_old:])
+    K, V = c.gather()
+    np.testing.assert_array_equal(K, V)                              # K and V follow one rule
+    s_new = c.k_scales[2].astype(np.float64)                         # page of the split (logical 0)
+    src = np.concatenate([held, x[n_old:ps]]).astype(np.float64)     # inputs of the split page
+    for h in range(H):
+        y = src[:, h] / s_new[h]
+        assert np.all(np.abs(K[:ps, h] / s_new[h] - y) <= _e4m3_half_step(y) * (1 + 1e-6))
+        assert np.all(np.abs(K[:n_old, h] - x[:n_old, h]) <=
+                      (_e4m3_half_step(x[:n_old, h] / s_old[h]) * s_old[h] +
+                       _e4m3_half_step(held[:, h] / s_new[h]) * s_new[h]) * (1 + 1e-6))
+    whole = oracle.PagedCacheFP8(H, D, ps, [2, 0, 1], 3)
+    whole.append(x, x)
+    np.testing.assert_array_equal(c.k_codes[[0, 1]], whole.k_codes[[0, 1]])
+    np.testing.assert_array_equal(c.k_scales[[0, 1]], whole.k_scales[[0, 1]])
