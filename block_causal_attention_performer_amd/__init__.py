@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.bca_workspace_bytes.restype = sz
     L.bca_status_string.argtypes = [i32]
     L.bca_status_string.restype = ctypes.c_char_p
+    L.performer_unit_noalloc.argtypes = [cp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp]
+    L.performer_unit_noalloc.restype = i32
     L.bca_session_create.argtypes = [cp, ctypes.POINTER(i32), i32, ctypes.POINTER(vp)]
     L.bca_session_create.restype = i32
     L.bca_session_unit.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, sz, i32, vp]
@@ -90,7 +92,10 @@ def lib() -> ctypes.CDLL:
     return L
 
 
+NOALLOC_SCRATCH_BYTES = 256 << 20       # BCA_NOALLOC_SCRATCH_BYTES
+
 EXPORTS = ("kv_append", "block_causal_attn", "fm_euler_step", "performer_unit",
+           "performer_unit_noalloc",
            "bca_workspace_bytes", "bca_status_string", "bca_session_create", "bca_session_unit",
            "bca_session_free_pages", "bca_session_destroy")
 
@@ -360,6 +365,21 @@ def performer_unit(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: 
         ctypes.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), q.shape[0], _ptr(w), _ptr(z),
         z.shape[1], n_steps, _ptr(o_scratch), wp, wb, ev, _stream(stream))
     _check(st, "performer_unit")
+    return z
+
+
+def performer_unit_noalloc(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                           q: torch.Tensor, w: torch.Tensor, z: torch.Tensor, n_steps: int,
+                           o_scratch: torch.Tensor, stream=None) -> torch.Tensor:
+    """performer_unit through the entry point that allocates nothing: its
+    scratch is the library's fixed per-GPU array (NOALLOC_SCRATCH_BYTES).
+    Calls that overlap on one GPU race on that array."""
+    _check_unit(cache, k_new, v_new, q, w, z, o_scratch)
+    cache.require_mapped(cache.n_tokens + q.shape[0], "performer_unit_noalloc")
+    st = lib().performer_unit_noalloc(
+        ctypes.byref(cache.c), _ptr(k_new), _ptr(v_new), _ptr(q), q.shape[0], _ptr(w), _ptr(z),
+        z.shape[1], n_steps, _ptr(o_scratch), _stream(stream))
+    _check(st, "performer_unit_noalloc")
     return z
 
 

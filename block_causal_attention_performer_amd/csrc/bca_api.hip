@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/bca.h: argument validation,
 // work-split heuristics and kernel dispatch.  Nothing here allocates device
-// memory; the only state kept between calls is a small host-side memo of
-// split decisions.
+// memory; the state kept between calls is a small host-side memo of split
+// decisions and, per GPU, the address of the fixed scratch array of
+// performer_unit_noalloc.
 #include <math.h>
 #include <string.h>
 
@@ -14,7 +15,37 @@
 
 using namespace bca;
 
+// Fixed scratch of performer_unit_noalloc, for callers that cannot allocate:
+// one copy per GPU the library runs on, in the code object's device data,
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host the name is a stand-in, not a device address): the
+// device address of each GPU's copy is looked up once, with that GPU
+// current, and kept in noalloc_ptr.
+static __device__ __align__(256) char scratch[BCA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[kMaxDevices];
+
+// Device address of the current GPU's scratch array.
+bca_status noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BCA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return BCA_EUNSUPPORTED;
+  std::lock_guard<std::mutex> g(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return BCA_EHIP;
+    }
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return BCA_OK;
+}
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int64_t x) { int l = 0; while ((int64_t{1} << l) < x) ++l; return l; }
@@ -557,6 +588,21 @@ bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void* v_new,
   if (st != BCA_OK) return st;
   return enqueue_performer(c, k_new, v_new, q, n_q, w, z, n_ch, n_steps, o_scratch, workspace,
                            workspace_bytes, attn_events, s);
+}
+
+bca_status performer_unit_noalloc(bca_kv_cache* c, const void* k_new, const void* v_new,
+                                  const void* q, int64_t n_q, const float* w, float* z,
+                                  int32_t n_ch, int32_t n_steps, void* o_scratch, hipStream_t s) {
+  bca_status st = check_performer(c, k_new, v_new, q, n_q, w, z, n_ch, n_steps, o_scratch);
+  if (st != BCA_OK) return st;
+  // the fast path's least need: the velocity partials and the attention
+  // flags and queue counters of an unsplit call
+  if (euler_ws_bytes(n_q) + attn_split_bytes(c, n_q, 1) > BCA_NOALLOC_SCRATCH_BYTES) return BCA_ERANGE;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != BCA_OK) return st;
+  return enqueue_performer(c, k_new, v_new, q, n_q, w, z, n_ch, n_steps, o_scratch, ws,
+                           BCA_NOALLOC_SCRATCH_BYTES, nullptr, s);
 }
 
 bca_status bca_session_create(bca_kv_cache* c, const int32_t* free_pages, int32_t n_free,

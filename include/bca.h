@@ -217,6 +217,31 @@ BCA_API bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void
                           hipEvent_t* attn_events, hipStream_t s);
 
 /*
+ * performer_unit_noalloc -- performer_unit for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  The same unit (same arguments and results as
+ * performer_unit without the workspace and the timing hook); it calls no
+ * allocator.  Its scratch is a fixed array of BCA_NOALLOC_SCRATCH_BYTES in
+ * the library's device data, one per GPU, which each GPU the library runs
+ * on holds until the process ends.  The key-range split of the attention
+ * takes as many splits as fit in it (3 at the v0.2 unit, 40 heads x 3712
+ * queries, instead of up to 8), so results can differ from performer_unit
+ * with a larger workspace by rounding; with a workspace of exactly
+ * BCA_NOALLOC_SCRATCH_BYTES performer_unit gives the same bits.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (the kernels need no initial contents): calls that overlap on one
+ * GPU -- on different streams, or from different threads, without ordering
+ * -- race on it and must not be made.
+ * Errors: as performer_unit; BCA_ERANGE when the unit's least scratch need
+ * (512 bytes per query for the velocity partials plus the attention's flags
+ * and counters) passes BCA_NOALLOC_SCRATCH_BYTES (about 500,000 queries).
+ */
+#define BCA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+BCA_API bca_status performer_unit_noalloc(bca_kv_cache* c, const void* k_new, const void* v_new,
+                                  const void* q, int64_t n_q, const float* w, float* z,
+                                  int32_t n_ch, int32_t n_steps, void* o_scratch, hipStream_t s);
+
+/*
  * Streaming session -- many consecutive performer units over one growing
  * cache (deep read section 4 step 3: the performer appends every received
  * slice to its own full-history cache and runs the solver for the next

@@ -229,3 +229,21 @@ def test_binding_tensor_checks():
         bca._need(torch.empty(4, device="meta"), "t", dev, (torch.float32,))
     with pytest.raises(ValueError, match="required"):
         bca._need(None, "t", dev, (torch.float32,))
+
+
+def test_performer_unit_noalloc_validates_on_the_host():
+    """The entry point that allocates nothing checks every argument, and that
+    the unit's least scratch need fits its fixed array, before any HIP call:
+    EINVAL for a bad argument, ERANGE for a unit of 600,000 queries (512
+    bytes each of velocity partials alone pass 256 MiB)."""
+    L = bca.lib()
+    c = _cache()
+    assert L.performer_unit_noalloc(ctypes.byref(c), FAKE, FAKE, FAKE, 16, FAKE, FAKE, 0, 4, FAKE,
+                                    None) == -1
+    assert L.performer_unit_noalloc(ctypes.byref(c), FAKE, FAKE, FAKE, 16, FAKE, FAKE, 16, 4, None,
+                                    None) == -1
+    big = _cache(max_logical_pages=4096, n_phys_pages=4096)
+    assert L.performer_unit_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, 600000, FAKE, FAKE, 16, 4,
+                                    FAKE, None) == -2
+    assert c.n_tokens == 0 and big.n_tokens == 0
+    assert bca.NOALLOC_SCRATCH_BYTES == 256 << 20
