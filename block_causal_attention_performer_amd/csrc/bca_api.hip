@@ -93,7 +93,6 @@ bca_status check_append(const bca_kv_cache* c, const void* k_new, const void* v_
   const int32_t want = c->dtype == BCA_F32 ? BCA_F32 : BCA_BF16;
   if (src_dtype != want) return BCA_EUNSUPPORTED;
   if (c->n_tokens + n_new > (int64_t)c->max_logical_pages * c->page_size) return BCA_ERANGE;
-  if (c->dtype == BCA_FP8_E4M3 && n_new > 0 && c->n_tokens % c->page_size != 0) return BCA_EUNSUPPORTED;
   return BCA_OK;
 }
 

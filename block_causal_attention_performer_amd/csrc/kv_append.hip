@@ -122,9 +122,24 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// One workgroup per (logical page touched, head).  Rows of the page that
-// the slice covers are [r0, r1); the page starts fresh (appends to an fp8
-// cache start at a page boundary), rows past r1 get code 0.
+// The values of rows a page already holds: its E4M3 codes (exact in fp32
+// through the hardware conversion) times the page's scale, rounded to fp32.
+__device__ __forceinline__ void held8(uint2 codes, float sc, float (&x)[8]) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, true);
+  x[0] = a[0] * sc; x[1] = a[1] * sc; x[2] = b[0] * sc; x[3] = b[1] * sc;
+  x[4] = c[0] * sc; x[5] = c[1] * sc; x[6] = d[0] * sc; x[7] = d[1] * sc;
+}
+
+// One workgroup per (logical page touched, head).  The slice fills rows
+// [n_old, r1) of the page; rows [0, n_old) (first page of an append that
+// starts inside a page) already hold codes, whose values enter the block as
+// they are held, so the whole page is quantised afresh over its valid rows;
+// rows past r1 get code 0.  Each thread reads the held codes of its own
+// 8-value chunk before it writes the chunk, and every thread reads the
+// page's old scale before the barrier after which thread 0 replaces it.
 template <int D>
 __global__ __launch_bounds__(kThreads) void append_fp8_kernel(AppendArgs a) {
   const int ps = 1 << a.ps_log2;
@@ -134,6 +149,7 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(AppendArgs a) {
   const int64_t t0 = lp << a.ps_log2;
   const int64_t r1l = a.n0 + a.n_new - t0;
   const int r1 = (int)(r1l < ps ? r1l : ps);
+  const int n_old = a.n0 > t0 ? (int)(a.n0 - t0) : 0;
   const int64_t page = a.page_table[lp];
   const uint16_t* src_k = static_cast<const uint16_t*>(a.k_new);
   const uint16_t* src_v = static_cast<const uint16_t*>(a.v_new);
@@ -144,36 +160,53 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(AppendArgs a) {
 
   for (int which = 0; which < 2; ++which) {
     const uint16_t* src = which == 0 ? src_k : src_v;
+    float* scales = which == 0 ? a.k_scales : a.v_scales;
+    const float old_sc = n_old > 0 ? scales[page * H + h] : 1.0f;
+    // the 8 values of row r, head dims 8c .. 8c+7, as the block holds them
+    auto row8 = [&](int r, int c, float (&x)[8]) {
+      if (r < n_old) {
+        uint2 codes;
+        if (which == 0) {
+          codes = *reinterpret_cast<const uint2*>(kp + (int64_t)r * D + c * 8);
+        } else {
+          uint32_t w[2] = {0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e >> 2] |= (uint32_t)vp[(int64_t)(c * 8 + e) * ps + r] << (8 * (e & 3));
+          codes = make_uint2(w[0], w[1]);
+        }
+        held8(codes, old_sc, x);
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + ((t0 - a.n0 + r) * H + h) * D + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(v[e] << 16);
+          x[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+        }
+      }
+    };
     // amax over the valid rows
     float amax = 0.0f;
     for (int i = threadIdx.x; i < r1 * (D / 8); i += kThreads) {
-      const int r = i / (D / 8), c = i % (D / 8);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + ((t0 - a.n0 + r) * H + h) * D + c * 8);
+      float x[8];
+      row8(i / (D / 8), i % (D / 8), x);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        amax = fmaxf(amax, fabsf(__uint_as_float(v[e] << 16)));
-        amax = fmaxf(amax, fabsf(__uint_as_float(v[e] & 0xFFFF0000u)));
-      }
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
     }
     amax = block_max_256(amax, red);
     const float scale = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
     const float inv = amax == 0.0f ? 0.0f : __fdiv_rn(448.0f, amax);
-    if (threadIdx.x == 0) {
-      float* sc = which == 0 ? a.k_scales : a.v_scales;
-      sc[page * H + h] = scale;
-    }
+    if (threadIdx.x == 0) scales[page * H + h] = scale;
     // codes: 8 values (one 16-byte bf16 vector) per thread per pass
     for (int i = threadIdx.x; i < ps * (D / 8); i += kThreads) {
       const int r = i / (D / 8), c = i % (D / 8);
       uint32_t dw[2] = {0u, 0u};             // codes 0..3, 4..7 (byte e of dw[e / 4])
       if (r < r1 && amax != 0.0f) {           // an all-zero block (-0 too) gets codes 0
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + ((t0 - a.n0 + r) * H + h) * D + c * 8);
+        float x[8];
+        row8(r, c, x);
 #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          dw[e >> 1] = e4m3x2_rne_sat<false>(__uint_as_float(v[e] << 16) * inv,
-                                             __uint_as_float(v[e] & 0xFFFF0000u) * inv, 0u);
-          dw[e >> 1] = e4m3x2_rne_sat<true>(__uint_as_float(v[e + 1] << 16) * inv,
-                                            __uint_as_float(v[e + 1] & 0xFFFF0000u) * inv, dw[e >> 1]);
+        for (int e = 0; e < 8; e += 4) {
+          dw[e >> 2] = e4m3x2_rne_sat<false>(x[e] * inv, x[e + 1] * inv, 0u);
+          dw[e >> 2] = e4m3x2_rne_sat<true>(x[e + 2] * inv, x[e + 3] * inv, dw[e >> 2]);
         }
       }
       if (which == 0) {
@@ -238,7 +271,8 @@ hipError_t launch_append_copy(const AppendArgs& a, int elem_bytes, hipStream_t s
 
 hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t s) {
   const int ps = 1 << a.ps_log2;
-  const int64_t npages = (a.n_new + ps - 1) / ps;   // n0 is page aligned
+  // logical pages from the one holding n0 to the one holding n0 + n_new - 1
+  const int64_t npages = ((a.n0 & (ps - 1)) + a.n_new + ps - 1) / ps;
   dim3 grid((unsigned)npages, (unsigned)a.n_heads);
   if (a.head_dim != 128 || ps > 256) return hipErrorInvalidValue;
   append_fp8_kernel<128><<<grid, kThreads, 0, s>>>(a);

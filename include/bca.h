@@ -116,8 +116,10 @@ typedef struct {
  * copy.  An fp8 cache quantises each touched (page, head) block of K and of
  * V: amax over its valid rows, scale = amax/448, code = RNE-saturate to
  * E4M3FN of (x * (448/amax)) in fp32; amax = 0 gives scale 1 and codes 0;
- * slots past the valid rows get code 0.  fp8 appends must start at a page
- * boundary (n_tokens % page_size == 0), else BCA_EUNSUPPORTED.
+ * slots past the valid rows get code 0.  An fp8 append that starts inside a
+ * partly filled page re-quantises that page: the rows it already holds
+ * enter its block as the values they hold, fp32(decode(code) * scale), so
+ * they may move by one rounding onto the new scale's grid.
  * n_new == 0 is a no-op.  BCA_ERANGE if the append would pass
  * max_logical_pages * page_size.
  */

@@ -68,8 +68,8 @@ def _append(c, n=10, src=bca.BF16, k=FAKE, v=FAKE):
     ({"n_heads": 0}, 10, bca.BF16, -1),
     ({"dtype": 7}, 10, bca.BF16, -3),
     ({"dtype": bca.FP8_E4M3}, 10, bca.BF16, -1),    # fp8 without scales
-    ({"dtype": bca.FP8_E4M3, "k_scales": FAKE, "v_scales": FAKE, "n_tokens": 100}, 10,
-     bca.BF16, -3),                                  # fp8 append not page aligned
+    ({"dtype": bca.FP8_E4M3, "k_scales": FAKE, "v_scales": FAKE, "head_dim": 64}, 10,
+     bca.BF16, -3),                                  # fp8 pages only for head dim 128
     ({"dtype": bca.FP8_E4M3, "k_scales": FAKE, "v_scales": FAKE, "page_size": 16}, 10,
      bca.BF16, -3),
 ])
