@@ -91,16 +91,28 @@ def _traffic():
         return None
 
 
-def cpu_baseline(inp, w, rows_n, heads_n):
-    """Time the float64 oracle on rows_n query rows x heads_n heads over the
-    whole key range (same inputs as the GPU step)."""
+def _cpu_model():
+    """Host CPU as lscpu names it (model, sockets, cores per socket)."""
+    info = {}
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            info[k.strip()] = v.strip()
+    except Exception:  # pragma: no cover
+        pass
+    return {"model": info.get("Model name"), "sockets": info.get("Socket(s)"),
+            "cores_per_socket": info.get("Core(s) per socket"),
+            "threads_per_core": info.get("Thread(s) per core"), "logical_cpus": info.get("CPU(s)")}
+
+
+def _oracle_attention_sample(inp, w, rows_n, heads_n):
+    """Seconds and FLOPs of the float64 oracle on rows_n query rows x heads_n
+    heads of the workload's unit over its whole key range (every key is
+    visible to the unit's queries)."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     H = w.n_heads
     rows = np.linspace(0, w.unit_tokens - 1, rows_n).astype(np.int64)
     heads = np.arange(0, H, max(1, H // heads_n))[:heads_n]
@@ -109,14 +121,100 @@ def cpu_baseline(inp, w, rows_n, heads_n):
     k = torch.cat([inp["k_hist"][:, hsel], inp["k_new"][:, hsel]]).float().cpu().numpy().astype(np.float64)
     v = torch.cat([inp["v_hist"][:, hsel], inp["v_new"][:, hsel]]).float().cpu().numpy().astype(np.float64)
     t0 = time.perf_counter()
-    oracle.attention_dense(q, k, v, w.n_hist, w.unit_tokens, rows=rows)
-    del q, k, v
+    oracle.attention_dense(q, k, v, rows=rows)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.head_dim * len(rows) * len(heads) * w.n_kv
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"attention_dense (float64 numpy) of {len(rows)} query rows x {len(heads)} "
-                      f"heads over all {w.n_kv} keys of the {w.name} workload's unit; {dt:.2f} s",
-            "seconds": dt}
+    return dt, 4.0 * w.head_dim * len(rows) * len(heads) * w.n_kv, len(rows), len(heads)
+
+
+def cpu_baseline(inp, w, rows_n, heads_n, workloads):
+    """The float64 oracle (numpy, as it stands) timed on the host: the
+    workload's attention on rows_n query rows x heads_n heads with every
+    BLAS thread (the reported value), the same on a 32-row sample with one
+    thread, and an all-thread sample of the v0.1 unit's attention; each as
+    TFLOP/s of the same FLOP count as the GPU figure, plus the unit's four
+    attention calls extrapolated to the whole unit at the all-thread rate."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    dt, fl, nr, nh = _oracle_attention_sample(inp, w, rows_n, heads_n)
+    with threadpool_limits(limits=1):
+        dt1, fl1, nr1, nh1 = _oracle_attention_sample(inp, w, 32, heads_n)
+    w1 = workloads.WORKLOADS["v01_unit"]
+    inp1 = workloads.make_unit_inputs(w1, device=inp["q"].device)
+    dtc, flc, nrc, nhc = _oracle_attention_sample(inp1, w1, 256, w1.n_heads)
+    del inp1
+    rate = fl / dt
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"attention_dense (float64 numpy) of {nr} query rows x {nh} heads over all "
+                      f"{w.n_kv} keys of the {w.name} workload's unit; {dt:.2f} s",
+            "seconds": dt,
+            "cpu": _cpu_model(),
+            "one_thread": {"value": fl1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": dt1,
+                           "sample": f"{nr1} query rows x {nh1} heads, same keys"},
+            "v01_unit": {"value": flc / dtc / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+                         "seconds": dtc,
+                         "sample": f"{nrc} query rows x {nhc} heads over all {w1.n_kv} keys of the "
+                                   f"v01_unit workload's unit"},
+            "unit_attention_s_extrapolated": w.n_steps * w.attn_flops() / rate}
+
+
+class ClockSampler:
+    """Samples the GPU's GFX clock (amdsmi GPU metrics: current_gfxclk per
+    XCC, and the firmware's average_gfxclk_frequency) every 10 ms from a
+    background thread while the timed steps run.  Reports None fields when
+    amdsmi is unavailable."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.avg = [], []
+        self._stop = threading.Event()
+        self._t = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            self._smi = None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                cur = m.get("current_gfxclks")
+                vals = [c for c in cur if isinstance(c, (int, float)) and 0 < c < 10000] if isinstance(cur, list) else []
+                if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+                    vals = [m["current_gfxclk"]]
+                if vals:
+                    self.samples.append(sum(vals) / len(vals))
+                a = m.get("average_gfxclk_frequency")
+                if isinstance(a, (int, float)) and 0 < a < 10000:
+                    self.avg.append(a)
+            except Exception:
+                pass
+            self._stop.wait(0.01)
+
+    def __enter__(self):
+        if self._smi is not None:
+            import threading
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t is not None:
+            self._t.join()
+
+    def report(self):
+        s = sorted(self.samples)
+        out = {"source": "amdsmi GPU metrics during the timed steps (current_gfxclk per XCC, mean over XCCs)",
+               "samples": len(s), "mean_mhz": None, "min_mhz": None, "max_mhz": None,
+               "firmware_average_mhz": None}
+        if s:
+            out.update(mean_mhz=round(sum(s) / len(s), 1), min_mhz=s[0], max_mhz=s[-1])
+        if self.avg:
+            out["firmware_average_mhz"] = round(sum(self.avg) / len(self.avg), 1)
+        return out
 
 
 def catchup(args, w, inp, cache, hip, stream, bca, workloads):
@@ -321,12 +419,14 @@ def main():
     torch.cuda.synchronize()
     evs = [[hip.event() for _ in range(3 * S)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    clocks = ClockSampler()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_unit = wall * 1e3 / args.steps
     # main attention kernel (the roofline's kernel) and the whole call
     # (with the split combine and the exact rerun of flagged tiles)
@@ -411,6 +511,7 @@ def main():
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "attn_call_ms": round(call_avg, 4),
         "attn_call_tflops": round(flops_call / (call_avg * 1e-3) / 1e12, 2),
+        "gfx_clock": clocks.report(),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -432,7 +533,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_rows, args.cpu_heads)
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_rows, args.cpu_heads, workloads)
     print(json.dumps(out), flush=True)
 
 

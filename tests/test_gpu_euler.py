@@ -32,7 +32,9 @@ def test_exact_velocity_reproduces_interpolant():
     assert_close(np64(z), z0.double().numpy(), 1e-4, what="z(0) == z0")
 
 
-@pytest.mark.parametrize("n_tok,H,D", [(3712, 40, 128), (1024, 24, 128), (77, 4, 64), (5, 1, 64)])
+@pytest.mark.parametrize("n_tok,H,D", [(3712, 40, 128), (1024, 24, 128), (77, 4, 64), (5, 1, 64),
+                                        (1000, 40, 128), (17, 8, 64), (33, 12, 128), (5, 64, 128),
+                                        (40, 16, 64)])
 @pytest.mark.parametrize("with_ws", [True, False])
 def test_bf16_projection(n_tok, H, D, with_ws):
     k = H * D
@@ -89,3 +91,26 @@ def test_projection_workspace_contents_do_not_matter():
                 x.double().cpu().numpy().reshape(n_tok, H, D), w.double().cpu().numpy())
             assert_close(np64(z), want, 2e-2, what="two steps from a junk workspace")
         assert torch.equal(z, ref)
+
+
+@pytest.mark.parametrize("n_tok,k", [(3712, 5120), (1000, 3072), (9, 512)])
+def test_projection_is_deterministic(n_tok, k):
+    """The projection (k split in eighths, partials added in a fixed order)
+    gives the same bits call after call, with or without a workspace (the
+    matrix-core path or the fp32 vector path); ragged last row blocks (1000
+    and 9 tokens) included."""
+    x = workloads.randn((n_tok, k), 21, 0.05).to(torch.bfloat16).cuda()
+    w = workloads.randn((k, 16), 22).cuda()
+    z0 = workloads.randn((n_tok, 16), 23).cuda()
+    c = bca.KVCache(1, 128, 256, torch.zeros(1, dtype=torch.int32), 1, "bf16")
+    ws = bca.alloc_workspace(bca.workspace_bytes(c, n_tok, n_tok))
+    outs = []
+    for _ in range(3):
+        z = z0.clone()
+        bca.fm_euler_step(z, x, w, 0.25, workspace=ws)
+        outs.append(z)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    want = z0.double().cpu().numpy() - 0.25 * oracle.velocity(x.double().cpu().numpy(),
+                                                              w.double().cpu().numpy())
+    assert_close(np64(outs[0]), want, 1e-4, what="projection")
