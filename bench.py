@@ -158,37 +158,58 @@ def cpu_baseline(inp, w, rows_n, heads_n, workloads):
 
 
 class ClockSampler:
-    """Samples the GPU's GFX clock (amdsmi GPU metrics: current_gfxclk per
-    XCC, and the firmware's average_gfxclk_frequency) every 10 ms from a
-    background thread while the timed steps run.  Reports None fields when
-    amdsmi is unavailable."""
+    """Samples the GPU's GFX clock every 10 ms from a background thread while
+    the timed steps run, from two amdsmi sources: the GPU metrics table
+    (current_gfxclk per XCC, averaged over the XCCs) and the clock query
+    (amdsmi_get_clock_info, GFX domain).  Both are the firmware's
+    instantaneous readings, so the report gives medians and the 10th/90th
+    percentiles rather than means.  Fields are None when amdsmi is
+    unavailable."""
 
     def __init__(self):
         import threading
-        self.samples, self.avg = [], []
+        self.metrics, self.clk = [], []
         self._stop = threading.Event()
         self._t = None
+        self.device_bdf = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
-            self._smi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            # amdsmi lists every GPU of the host; take the one this process
+            # runs on (device 0), matched by its PCI domain and bus
+            p = torch.cuda.get_device_properties(0)
+            self._h = None
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+                dom, bus = bdf.split(":")[0], bdf.split(":")[1]
+                if int(dom, 16) == p.pci_domain_id and int(bus, 16) == p.pci_bus_id:
+                    self._h, self.device_bdf = h, bdf
+                    break
+            self._smi = amdsmi if self._h is not None else None
         except Exception:
             self._smi = None
 
+    @staticmethod
+    def _ok(x):
+        return isinstance(x, (int, float)) and 0 < x < 10000
+
     def _run(self):
+        smi = self._smi
         while not self._stop.is_set():
             try:
-                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                m = smi.amdsmi_get_gpu_metrics_info(self._h)
                 cur = m.get("current_gfxclks")
-                vals = [c for c in cur if isinstance(c, (int, float)) and 0 < c < 10000] if isinstance(cur, list) else []
-                if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+                vals = [c for c in cur if self._ok(c)] if isinstance(cur, list) else []
+                if not vals and self._ok(m.get("current_gfxclk")):
                     vals = [m["current_gfxclk"]]
                 if vals:
-                    self.samples.append(sum(vals) / len(vals))
-                a = m.get("average_gfxclk_frequency")
-                if isinstance(a, (int, float)) and 0 < a < 10000:
-                    self.avg.append(a)
+                    self.metrics.append(sum(vals) / len(vals))
+            except Exception:
+                pass
+            try:
+                c = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX).get("clk")
+                if self._ok(c):
+                    self.clk.append(c)
             except Exception:
                 pass
             self._stop.wait(0.01)
@@ -205,16 +226,20 @@ class ClockSampler:
         if self._t is not None:
             self._t.join()
 
+    @staticmethod
+    def _stats(v):
+        if not v:
+            return {"samples": 0, "median_mhz": None, "p10_mhz": None, "p90_mhz": None}
+        v = sorted(v)
+        q = lambda f: v[min(len(v) - 1, int(f * len(v)))]
+        return {"samples": len(v), "median_mhz": round(q(0.5), 1), "p10_mhz": round(q(0.1), 1),
+                "p90_mhz": round(q(0.9), 1)}
+
     def report(self):
-        s = sorted(self.samples)
-        out = {"source": "amdsmi GPU metrics during the timed steps (current_gfxclk per XCC, mean over XCCs)",
-               "samples": len(s), "mean_mhz": None, "min_mhz": None, "max_mhz": None,
-               "firmware_average_mhz": None}
-        if s:
-            out.update(mean_mhz=round(sum(s) / len(s), 1), min_mhz=s[0], max_mhz=s[-1])
-        if self.avg:
-            out["firmware_average_mhz"] = round(sum(self.avg) / len(self.avg), 1)
-        return out
+        return {"source": "amdsmi during the timed steps, every 10 ms (firmware instantaneous readings)",
+                "device_bdf": self.device_bdf,
+                "gpu_metrics_current_gfxclk": self._stats(self.metrics),
+                "clock_info_gfx": self._stats(self.clk)}
 
 
 def catchup(args, w, inp, cache, hip, stream, bca, workloads):

@@ -516,14 +516,17 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       if (!idle) {
         const int64_t k0 = (int64_t)t * BN;
         if (k0 + BN > lim_first) {
-          const int lrel = (int)min(lim - k0, (int64_t)BN);
+          // key 32 mb + 16 (rr / 8) + 8 half + rr % 8 is masked when it is
+          // >= lrel: compare the lane-independent part (an inline constant)
+          // with lrel - 8 half, so no per-element key index is held in a
+          // register across the loop
+          int thr = (int)min(lim - k0, (int64_t)BN) - 8 * half;
+          asm volatile("" : "+v"(thr));
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-              const int key = 32 * mb + 16 * (rr >> 3) + 8 * half + (rr & 7);
-              if (key >= lrel) s[mb][rr] = -INFINITY;
-            }
+            for (int rr = 0; rr < 16; ++rr)
+              if (32 * mb + 16 * (rr >> 3) + (rr & 7) >= thr) s[mb][rr] = -INFINITY;
         }
         // fp8: the K scale of tile t multiplies its logits; its V scale
         // multiplies P(t) (folded into the exponent), the row sum is
@@ -649,21 +652,20 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
         }
       }
   } else {
+    // the split's output over its keys, normalised by its own row sum, in
+    // bf16 (the merge weighs it by l 2^(m - M)); an empty split stores zeros
     const int64_t prow = (int64_t)split * a.n_q + qrow;
-    float* op = a.ws_o + (prow * H + h) * D;
+    uint16_t* op = a.ws_o + (prow * H + h) * D;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
         const int d = 32 * db + 16 * run + 8 * half;
-        f32x4 x0, x1;
+        bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x0[e] = o[db][8 * run + e];
-          x1[e] = o[db][8 * run + 4 + e];
-        }
-        *reinterpret_cast<f32x4*>(op + d) = x0;
-        *reinterpret_cast<f32x4*>(op + d + 4) = x1;
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)(o[db][8 * run + e] * inv);
+        *reinterpret_cast<bf16x8*>(op + d) = v;
       }
     if (half == 0) {
       float* ml = a.ws_ml + (prow * H + h) * 2;

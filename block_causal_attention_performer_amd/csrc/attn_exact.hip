@@ -435,21 +435,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_exact_kernel(AttnArgs a) {
         }
       }
     } else {
+      // normalised by the split's row sum, in bf16, as the merge reads it
       const int64_t prow = (int64_t)split * a.n_q + qrow[nb];
-      float* op = a.ws_o + (prow * H + h) * D;
+      uint16_t* op = a.ws_o + (prow * H + h) * D;
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int run = 0; run < 2; ++run) {
           const int d = 32 * db + 16 * run + 8 * half;
-          f32x4 x0, x1;
+          bf16x8 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x0[e] = o[db][nb][8 * run + e];
-            x1[e] = o[db][nb][8 * run + 4 + e];
-          }
-          *reinterpret_cast<f32x4*>(op + d) = x0;
-          *reinterpret_cast<f32x4*>(op + d + 4) = x1;
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)(o[db][nb][8 * run + e] * inv);
+          *reinterpret_cast<bf16x8*>(op + d) = v;
         }
       if (half == 0) {
         float* ml = a.ws_ml + (prow * H + h) * 2;

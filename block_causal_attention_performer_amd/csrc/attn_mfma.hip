@@ -435,21 +435,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     }
   } else {
+    // the split's output normalised by its own row sum, in bf16; an empty
+    // split stores zeros
     const int64_t prow = (int64_t)split * a.n_q + qrow;
-    float* op = a.ws_o + (prow * H + h) * D;
+    uint16_t* op = a.ws_o + (prow * H + h) * D;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
         const int d = 32 * db + 16 * run + 8 * half;
-        f32x4 x0, x1;
+        bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x0[e] = o[db][8 * run + e];
-          x1[e] = o[db][8 * run + 4 + e];
-        }
-        *reinterpret_cast<f32x4*>(op + d) = x0;
-        *reinterpret_cast<f32x4*>(op + d + 4) = x1;
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)(o[db][8 * run + e] * inv);
+        *reinterpret_cast<bf16x8*>(op + d) = v;
       }
     if (half == 0) {
       float* ml = a.ws_ml + (prow * H + h) * 2;
@@ -479,7 +478,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     ml[s] = *reinterpret_cast<const float2*>(a.ws_ml + (s * stride + item) * 2);
-    os[s] = *reinterpret_cast<const vec*>(a.ws_o + (s * stride + item) * D + lane * PER);
+    const uint16_t* src = a.ws_o + (s * stride + item) * D + lane * PER;
+    if constexpr (PER == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(src);
+      os[s] = vec{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+    } else {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(src);
+      os[s] = vec{__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)};
+    }
   }
   float M = -INFINITY;
 #pragma unroll
@@ -488,8 +495,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   float L = 0.0f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float w = ml[s].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[s].x - M);
-    L += w * ml[s].y;
+    // partial s holds its output normalised by its row sum l: its weight
+    // is l * 2^(m - M)
+    const float w = ml[s].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[s].x - M) * ml[s].y;
+    L += w;
     acc += w * os[s];
   }
   const float inv = 1.0f / L;

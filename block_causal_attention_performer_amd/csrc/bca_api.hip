@@ -133,7 +133,7 @@ size_t attn_flag_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
 }
 size_t attn_split_bytes(const bca_kv_cache* c, int64_t n_q, int nsplit) {
   const size_t per = (size_t)nsplit * n_q * c->n_heads;
-  const size_t parts = nsplit > 1 ? align256(per * c->head_dim * 4) + align256(per * 2 * 4) : 0;
+  const size_t parts = nsplit > 1 ? align256(per * c->head_dim * 2) + align256(per * 2 * 4) : 0;
   return attn_flag_bytes(c, n_q, nsplit) + kAttnSchedBytes + parts;
 }
 
@@ -153,7 +153,7 @@ bool attn_persistent(const bca_kv_cache* c) {
 // workgroup takes the next item of its own queue, else of the first later
 // queue with items left.  An item costs its key tiles times the per-tile
 // time of a CU under full load (fewer when its query tile has idle waves)
-// plus a fixed per-item cost; the combine reads s fp32 partials and writes
+// plus a fixed per-item cost; the combine reads s bf16 partials and writes
 // the output at a plain copy's rate.  The constants are measured on MI355X
 // (v0.2 launch: 1.63 us per 64-key tile per CU, about 6 us per item).
 double persistent_cost_us(const std::vector<int64_t>& qt_tiles, const std::vector<double>& qt_frac,
@@ -223,7 +223,7 @@ double persistent_cost_us(const std::vector<int64_t>& qt_tiles, const std::vecto
     ht[i] = t_new;
     hw[i] = w_new;
   }
-  const double comb = s == 1 ? 0.0 : ((double)s * n_q * H * D * 4 + (double)n_q * H * D * 2) / kCopyBytesPerUs;
+  const double comb = s == 1 ? 0.0 : ((double)s * n_q * H * D * 2 + (double)n_q * H * D * 2) / kCopyBytesPerUs;
   return end + comb;
 }
 
@@ -378,8 +378,8 @@ bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t bloc
     ws += kAttnSchedBytes;
     if (a.nsplit > 1) {
       const size_t per = (size_t)a.nsplit * n_q * c->n_heads;
-      a.ws_o = reinterpret_cast<float*>(ws);
-      a.ws_ml = reinterpret_cast<float*>(ws + align256(per * c->head_dim * 4));
+      a.ws_o = reinterpret_cast<uint16_t*>(ws);
+      a.ws_ml = reinterpret_cast<float*>(ws + align256(per * c->head_dim * 2));
     }
     e = launch_attn_mfma(a, fp8, main_done, s);
     if (e == hipSuccess) {

@@ -50,7 +50,8 @@ struct AttnArgs {
   const float* k_scales;
   const float* v_scales;
   const int32_t* page_table;
-  float* ws_o;       // split partials: [nsplit][n_q][H][D] fp32 (unnormalised)
+  uint16_t* ws_o;    // split partials: [nsplit][n_q][H][D] bf16, each split's output over
+                     // its keys normalised by its own row sum
   float* ws_ml;      // [nsplit][n_q][H][2]  (reference max in log2 units, row sum)
   int32_t* flags_out;    // fast kernel: [H][n_qtiles][nsplit][kAttnFlagWaves] overflow flags
   int32_t* sched;        // fast kernel: kAttnQueues work-queue counters (zeroed by its launch)

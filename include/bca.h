@@ -151,7 +151,9 @@ BCA_API bca_status kv_append(bca_kv_cache* c, const void* k_new, const void* v_n
  *        runs.  With it (layout: 512*n_q bytes, rounded up to a multiple of
  *        256, reserved for fm_euler_step's partial sums, then this call's
  *        region: overflow flags, 256 bytes of work-queue counters that the
- *        call zeroes itself, the fp32 split partials) a faster kernel runs
+ *        call zeroes itself, the split partials: per split, its output
+ *        normalised by its row sum in bf16 and its (m, l) in fp32) a
+ *        faster kernel runs
  *        that keeps the first key tile's row maximum as its softmax
  *        reference and flags any query tile in which a row's weights
  *        relative to that reference add up past 2^40 or to a non-finite

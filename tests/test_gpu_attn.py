@@ -162,11 +162,12 @@ def _split_ws_bytes(n_q, H, D, s):
     """Workspace bytes that hold block_causal_attn's region for at most s
     key-range splits: 512 bytes per query for fm_euler_step first, then the
     overflow flags (one int32 per 256-row query tile, head, split and wave
-    of 8), 256 bytes of queue counters and, for s > 1, the fp32 partials
-    O [s][n_q][H][D] and (m, l) [s][n_q][H][2], each part 256-aligned."""
+    of 8), 256 bytes of queue counters and, for s > 1, the partials: O
+    [s][n_q][H][D] in bf16 (normalised by each split's row sum) and (m, l)
+    [s][n_q][H][2] in fp32, each part 256-aligned."""
     a = lambda x: -(-x // 256) * 256
     flags = a(-(-n_q // 256) * H * s * 8 * 4)
-    parts = a(s * n_q * H * D * 4) + a(s * n_q * H * 2 * 4) if s > 1 else 0
+    parts = a(s * n_q * H * D * 2) + a(s * n_q * H * 2 * 4) if s > 1 else 0
     return a(512 * n_q) + flags + 256 + parts
 
 
