@@ -400,8 +400,8 @@ bca_status enqueue_attn(const void* q, int64_t n_q, int64_t q_pos0, int32_t bloc
 
 bca_status check_euler(float* z, const void* x, const float* w, int64_t n_tok, int32_t k,
                        int32_t n_ch, float dtau, int32_t x_dtype) {
-  if (!z || !x) return BCA_EINVAL;
   if (n_tok < 0 || n_ch <= 0 || !isfinite(dtau)) return BCA_EINVAL;
+  if (n_tok > 0 && (!z || !x)) return BCA_EINVAL;   // zero tokens touch nothing
   if (n_ch > 64) return BCA_EUNSUPPORTED;
   if (w) {
     if (k <= 0) return BCA_EINVAL;

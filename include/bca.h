@@ -176,7 +176,8 @@ BCA_API bca_status block_causal_attn(const void* q, int64_t n_q, int64_t q_pos0,
  * w != NULL: v[i][c] = sum_k x[i][k] * w[k][c], x [n_tok][k] (x_dtype BCA_BF16
  *            or BCA_F32), w [k][n_ch] fp32.
  * w == NULL: v = x, x [n_tok][n_ch] fp32 (k ignored).
- * z [n_tok][n_ch] fp32, updated in place.  n_ch <= 64.
+ * z [n_tok][n_ch] fp32, updated in place.  n_ch <= 64.  n_tok == 0 is a
+ * no-op (z and x may then be NULL).
  * workspace (may be NULL): with bf16 x, n_ch = 16, k a multiple of 256 and
  * at most 8192, and at least 512*n_tok bytes, the product runs on the
  * matrix cores (W split into bf16 high/low halves, W = hi + lo to ~2^-16;

@@ -120,11 +120,18 @@ def test_attn_rejects(kw, args, want):
     (dict(dtau=float("inf")), -1),
 ])
 def test_euler_rejects(args, want):
+    """Bad arguments; z or x NULL is refused only when there are tokens."""
     a = dict(z=FAKE, x=FAKE, w=FAKE, n_tok=10, k=64, n_ch=16, dtau=0.25, dtype=bca.BF16)
     a.update(args)
     st = bca.lib().fm_euler_step(a["z"], a["x"], a["w"], a["n_tok"], a["k"], a["n_ch"],
                                  a["dtau"], a["dtype"], None, 0, None)
     assert st == want
+
+
+def test_euler_zero_tokens_is_a_no_op():
+    L = bca.lib()
+    assert L.fm_euler_step(None, None, None, 0, 64, 16, 0.25, bca.F32, None, 0, None) == 0
+    assert L.fm_euler_step(None, FAKE, FAKE, 1, 64, 16, 0.25, bca.BF16, None, 0, None) == -1
 
 
 def test_performer_unit_validates_everything_first():
