@@ -228,12 +228,16 @@ class ClockSampler:
 
     @staticmethod
     def _stats(v):
+        # the first reading is taken as the thread starts, before the timed
+        # kernels have raised the clock: it is dropped; a handful of readings
+        # (a timed region of under 0.1 s) is flagged as not representative
+        v = sorted(v[1:])
         if not v:
-            return {"samples": 0, "median_mhz": None, "p10_mhz": None, "p90_mhz": None}
-        v = sorted(v)
+            return {"samples": 0, "median_mhz": None, "p10_mhz": None, "p90_mhz": None,
+                    "representative": False}
         q = lambda f: v[min(len(v) - 1, int(f * len(v)))]
         return {"samples": len(v), "median_mhz": round(q(0.5), 1), "p10_mhz": round(q(0.1), 1),
-                "p90_mhz": round(q(0.9), 1)}
+                "p90_mhz": round(q(0.9), 1), "representative": len(v) >= 10}
 
     def report(self):
         return {"source": "amdsmi during the timed steps, every 10 ms (firmware instantaneous readings)",

@@ -229,8 +229,8 @@ BCA_API bca_status performer_unit(bca_kv_cache* c, const void* k_new, const void
  * allocator.  Its scratch is a fixed array of BCA_NOALLOC_SCRATCH_BYTES in
  * the library's device data, one per GPU, which each GPU the library runs
  * on holds until the process ends.  The key-range split of the attention
- * takes as many splits as fit in it (3 at the v0.2 unit, 40 heads x 3712
- * queries, instead of up to 8), so results can differ from performer_unit
+ * may take only as many splits as fit in it (at most 6 at the v0.2 unit,
+ * 40 heads x 3712 queries, against up to 8), so results can differ from performer_unit
  * with a larger workspace by rounding; with a workspace of exactly
  * BCA_NOALLOC_SCRATCH_BYTES performer_unit gives the same bits.
  * Every call on one GPU shares that GPU's array and leaves its contents

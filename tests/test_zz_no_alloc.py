@@ -8,7 +8,8 @@ history is not a multiple of it).  Each must equal performer_unit:
     move z - eps likewise) when performer_unit gets the full workspace and
     may split further.
 The first unit has the v0.2 unit's 40 heads x 3712 queries, whose split
-partials (76 MB per split) the fixed 256 MiB hold only three of."""
+partials (bf16, 38 MB per split, plus 1.2 MB of row maxima and sums) the
+fixed 256 MiB hold at most six of, against the eight a full workspace allows."""
 import pytest
 import torch
 
