@@ -239,11 +239,23 @@ class ClockSampler:
         return {"samples": len(v), "median_mhz": round(q(0.5), 1), "p10_mhz": round(q(0.1), 1),
                 "p90_mhz": round(q(0.9), 1), "representative": len(v) >= 10}
 
-    def report(self):
-        return {"source": "amdsmi during the timed steps, every 10 ms (firmware instantaneous readings)",
-                "device_bdf": self.device_bdf,
-                "gpu_metrics_current_gfxclk": self._stats(self.metrics),
-                "clock_info_gfx": self._stats(self.clk)}
+    def report(self, achieved_tflops=None):
+        """achieved_tflops: the main kernel's rate.  One wave per SIMD issues
+        a 32x32x16 bf16 MFMA at most every 32 shader cycles, so that rate
+        needs a clock of at least achieved / 2500 * 2400 MHz; a median below
+        it cannot be the clock the kernel ran at (some hosts' firmware
+        tables report a stale or idle value), and `plausible` says so."""
+        out = {"source": "amdsmi during the timed steps, every 10 ms (firmware instantaneous readings)",
+               "device_bdf": self.device_bdf,
+               "gpu_metrics_current_gfxclk": self._stats(self.metrics),
+               "clock_info_gfx": self._stats(self.clk)}
+        if achieved_tflops is not None:
+            need = achieved_tflops / PEAK_BF16_TFLOPS * 2400.0
+            out["min_clock_mhz_for_rate"] = round(need, 1)
+            for key in ("gpu_metrics_current_gfxclk", "clock_info_gfx"):
+                med = out[key]["median_mhz"]
+                out[key]["plausible"] = med is not None and med >= 0.97 * need
+        return out
 
 
 def catchup(args, w, inp, cache, hip, stream, bca, workloads):
@@ -540,7 +552,7 @@ def main():
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "attn_call_ms": round(call_avg, 4),
         "attn_call_tflops": round(flops_call / (call_avg * 1e-3) / 1e12, 2),
-        "gfx_clock": clocks.report(),
+        "gfx_clock": clocks.report(attn_tflops),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
