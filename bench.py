@@ -132,7 +132,8 @@ def cpu_baseline(inp, w, rows_n, heads_n, workloads):
     BLAS thread (the reported value), the same on a 32-row sample with one
     thread, and an all-thread sample of the v0.1 unit's attention; each as
     TFLOP/s of the same FLOP count as the GPU figure, plus the unit's four
-    attention calls extrapolated to the whole unit at the all-thread rate."""
+    attention calls (and those of the long fp8 history's unit) extrapolated
+    at the all-thread rate."""
     from threadpoolctl import threadpool_info, threadpool_limits
     cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     dt, fl, nr, nh = _oracle_attention_sample(inp, w, rows_n, heads_n)
@@ -154,7 +155,12 @@ def cpu_baseline(inp, w, rows_n, heads_n, workloads):
                          "seconds": dtc,
                          "sample": f"{nrc} query rows x {nhc} heads over all {w1.n_kv} keys of the "
                                    f"v01_unit workload's unit"},
-            "unit_attention_s_extrapolated": w.n_steps * w.attn_flops() / rate}
+            "unit_attention_s_extrapolated": w.n_steps * w.attn_flops() / rate,
+            "long_fp8_unit_attention_s_extrapolated": {
+                "value": w.n_steps * workloads.WORKLOADS["v02_long_fp8"].attn_flops() / rate,
+                "basis": "the four attention calls of the long fp8 unit (2,787,712 keys) at the "
+                         "all-thread rate above: the oracle's dense attention does the same work "
+                         "per key whatever the cache dtype; decoding the E4M3 pages is not included"}}
 
 
 class ClockSampler:
