@@ -431,311 +431,311 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
     // and the softmax fills the gaps.
 
     if constexpr (FP8) {
-    // fp8: three-slot rings, two barriers per tile.  Iteration t with ring
-    // position R = (t - t0) % 3: K(t) and V(t) in slot R, V(t-1) in slot
-    // R+2 (mod 3), which also receives K(t+2) and V(t+2) during the vector
-    // phase; group B runs one phase behind group A.
-    // prologue: K(t0), K(t0+1) into the fp8 K ring (group A); V(t0), V(t0+1)
-    // into the fp8 V ring, zeros into bf16 V slot 2, which stands for
-    // V(t0-1) (group B); P(t0-1) = 0, so the first PV step adds exact zeros.
-    float sc[3] = {1.0f, 1.0f, 1.0f};      // scale of the tile staged into each slot
-    sc[0] = stage8(t0, fslot(ic<0>{}));
-    sc[1] = stage8(min(t0 + 1, tl), fslot(ic<1>{}));
-    if (group_b) {
-      const int gt = tid & (GT - 1);
+      // fp8: three-slot rings, two barriers per tile.  Iteration t with ring
+      // position R = (t - t0) % 3: K(t) and V(t) in slot R, V(t-1) in slot
+      // R+2 (mod 3), which also receives K(t+2) and V(t+2) during the vector
+      // phase; group B runs one phase behind group A.
+      // prologue: K(t0), K(t0+1) into the fp8 K ring (group A); V(t0), V(t0+1)
+      // into the fp8 V ring, zeros into bf16 V slot 2, which stands for
+      // V(t0-1) (group B); P(t0-1) = 0, so the first PV step adds exact zeros.
+      float sc[3] = {1.0f, 1.0f, 1.0f};      // scale of the tile staged into each slot
+      sc[0] = stage8(t0, fslot(ic<0>{}));
+      sc[1] = stage8(min(t0 + 1, tl), fslot(ic<1>{}));
+      if (group_b) {
+        const int gt = tid & (GT - 1);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lv2 + (i * GT + gt) * 16) = u32x4{0, 0, 0, 0};
-    }
-    wait_vm<0>();
-    // V: widened (t0 + 1 in matrix phase t0); K: read as fp8, only its scale
-    if (group_b) widen(t0, fslot(ic<0>{}), lv0, sc[0], 0);
-    else if ((tid & (GT - 1)) == 0) scl[0][0] = sc[0];
-    lds_barrier();
-    if (group_b) lds_barrier();            // group B runs one phase behind
-
-    auto iter = [&](int t, auto R) {
-      constexpr int r = decltype(R)::value;
-      constexpr int rp = (r + 2) % 3;
-      char* kl = k8slot(ic<r>{});
-      char* vprev = vslot(ic<rp>{});
-      // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T
-      f32x16 s[2];
-      __builtin_amdgcn_s_setprio(2);
-      if (!idle) {
-        // opaque per-iteration copies: keep the read addresses from being
-        // precomputed for all three slots outside the loop
-        uint32_t xk = kx8, xv = vx, kro = krow8, vro = vrow;
-        asm volatile("" : "+v"(xk), "+v"(xv), "+v"(kro), "+v"(vro));
-        const char* kbase = kl + kro;
-        const char* vbase = vprev + vro;
-        constexpr int NK = 8;                // (mb, kk, 16-byte part)
-        constexpr int NR = NK + 4 * DB;
-        auto rd = [&](int j) -> bf16x8 {
-          if (j < NK) {
-            const int mb = j >> 2, kk = (j >> 1) & 1, part = j & 1;
-            return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)((4 * kk + part) * 16)) ^ xk) + mb * 32 * 128));
-          }
-          const int c = (j - NK) / DB, db = (j - NK) % DB;
-          return __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
-        };
-        bf16x8 fr[NR];
-#pragma unroll
-        for (int j = 0; j < NIF; ++j) fr[j] = rd(j);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-          if (j < NK) {
-            if (j & 1) {                     // both halves of the (mb, kk) fragment read
-              const int mb = j >> 2, kk = (j >> 1) & 1;
-              const i32x8 af = __builtin_bit_cast(
-                  i32x8, __builtin_shufflevector(__builtin_bit_cast(u32x4, fr[j - 1]), __builtin_bit_cast(u32x4, fr[j]),
-                                                 0, 1, 2, 3, 4, 5, 6, 7));
-              s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qh[kk], kk == 0 ? f32x16{} : s[mb],
-                                                                       0, 0, 0, 127, 0, 127);
-              s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, ql[kk], s[mb], 0, 0, 0, 127, 0, 127);
-            }
-          } else {
-            const int c = (j - NK) / DB, db = (j - NK) % DB;
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
-          }
-          if (j + NIF < NR) fr[j + NIF] = rd(j + NIF);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lv2 + (i * GT + gt) * 16) = u32x4{0, 0, 0, 0};
       }
-      __builtin_amdgcn_s_setprio(0);
-      // widen tile t+1 (staged one vector phase ago) into its bf16 slot,
-      // which held tile t-2; the matrix group reaches this barrier before
-      // the vector group, so the work fills its wait
       wait_vm<0>();
-      if (group_b) widen(min(t + 1, tl), fslot(ic<r + 1>{}), vslot(ic<(r + 1) % 3>{}), sc[(r + 1) % 3], (r + 1) % 3);
-      else if ((tid & (GT - 1)) == 0) scl[0][(r + 1) % 3] = sc[(r + 1) % 3];
+      // V: widened (t0 + 1 in matrix phase t0); K: read as fp8, only its scale
+      if (group_b) widen(t0, fslot(ic<0>{}), lv0, sc[0], 0);
+      else if ((tid & (GT - 1)) == 0) scl[0][0] = sc[0];
       lds_barrier();
+      if (group_b) lds_barrier();            // group B runs one phase behind
 
-      // ---------------- vector phase: next tile two ahead into the free
-      // slot, then the softmax of tile t -> P(t)
-      sc[(r + 2) % 3] = stage8(min(t + 2, tl), fslot(ic<r + 2>{}));
-      if (!idle) {
-        const int64_t k0 = (int64_t)t * BN;
-        if (k0 + BN > lim_first) {
-          int thr = (int)min(lim - k0, (int64_t)BN) - 8 * half;
-          asm volatile("" : "+v"(thr));
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-              if (32 * mb + 16 * (rr >> 3) + (rr & 7) >= thr) s[mb][rr] = -INFINITY;
-        }
-        // the K scale of tile t multiplies its logits; its V scale
-        // multiplies P(t) (folded into the exponent), the row sum is
-        // divided by it back
-        const float sl = a.scale_log2 * scl[0][r] * qs;
-        if (t == t0) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
-          m_run = pair_max(mx) * sl;
-        }
-        const float mneg = __builtin_amdgcn_logf(scl[1][r]) - m_run;
-        float part[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int mb = c >> 1, rb = 8 * (c & 1);
-          float acc = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
-            acc += p;
-            pp[c][e] = (__bf16)p;
-          }
-          part[c] = acc;
-        }
-        // the tile's own V scale divides its sum back out
-        float tsum = (part[0] + part[1]) + (part[2] + part[3]);
-        tsum *= __builtin_amdgcn_rcpf(scl[1][r]);
-        overflow |= !(tsum <= kSlowSum);
-        l_run += tsum;
-      }
-      lds_barrier();
-    };
-
-    int t = t0;
-    for (; t + 2 <= tl; t += 3) {
-      iter(t, ic<0>{});
-      iter(t + 1, ic<1>{});
-      iter(t + 2, ic<2>{});
-    }
-    if (t <= tl) iter(t, ic<0>{});
-    if (t + 1 <= tl) iter(t + 1, ic<1>{});
-    final_pv(pp, (tl - t0) % 3);
-    if (tid == 0) item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
-    if (!group_b) lds_barrier();           // balance group B's extra barrier
-
-    } else {
-    // bf16: four-slot rings, tile t in slot (t - t0) % 4, one barrier per
-    // tile.  Between two barriers (window k) group A runs the vector phase
-    // of tile k and then the matrix phase of tile k+1, group B the matrix
-    // phase of tile k and then the vector phase of tile k, so the groups are
-    // in opposite phases without a barrier between the phases.  In window k
-    // group A stages K(k+3) and waits for K(k+2), group B stages V(k+2) and
-    // waits for V(k+1) (and clears its tail); the barrier ending the window
-    // publishes both.  The tiles read in window k are K(k), K(k+1), V(k-1)
-    // and V(k), none of them in a slot being staged into.
-    // prologue: K(t0..t0+2) into K slots 0..2 (group A); V(t0), V(t0+1) into
-    // V slots 0, 1 and zeros into V slot 3, which stands for V(t0-1) (group
-    // B); K(t0), K(t0+1) and V(t0) complete before the first barrier.
-    if (!group_b) {
-      stage(t0, lk0);
-      stage(min(t0 + 1, tl), lk1);
-      stage(min(t0 + 2, tl), lk2);
-      wait_vm<NL>();
-    } else {
-      stage(t0, lv0);
-      stage(min(t0 + 1, tl), lv1);
-      const int gt = tid & (GT - 1);
-#pragma unroll
-      for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lv3 + (i * GT + gt) * 16) = u32x4{0, 0, 0, 0};
-      wait_vm<NL>();
-      zero_tail(t0, lv0);
-    }
-    lds_barrier();
-
-    f32x16 s[2];
-    // matrix phase of tile t (ring position r): S(t) = K(t) Q^T, then
-    // O += V(t-1)^T P(t-1)^T
-    auto mat = [&](int t, auto R) {
-      constexpr int r = decltype(R)::value;
-      char* kl = kslot(ic<r>{});
-      char* vprev = vslot(ic<(r + 3) & 3>{});
-      __builtin_amdgcn_s_setprio(2);
-      if (!idle) {
-        // opaque per-phase copies: keep the read addresses from being
-        // precomputed for all four slots outside the loop
-        uint32_t xk = kx, xv = vx, kro = krow, vro = vrow;
-        asm volatile("" : "+v"(xk), "+v"(xv), "+v"(kro), "+v"(vro));
-        const char* kbase = kl + kro;
-        const char* vbase = vprev + vro;
-        constexpr int NK = 2 * KK;
-        constexpr int NR = NK + 4 * DB;
-        auto rd = [&](int j) -> bf16x8 {
-          if (j < NK) {
-            const int kk = j >> 1, mb = j & 1;
-            return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)(32 * kk)) ^ xk) + mb * 32 * D * 2));
-          }
-          const int c = (j - NK) / DB, db = (j - NK) % DB;
-          return __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
-        };
-        bf16x8 fr[NR];
-#pragma unroll
-        for (int j = 0; j < NIF; ++j) fr[j] = rd(j);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-          if (j < NK) {
-            const int kk = j >> 1, mb = j & 1;
-            s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[kk], kk == 0 ? f32x16{} : s[mb], 0, 0, 0);
-          } else {
+      auto iter = [&](int t, auto R) {
+        constexpr int r = decltype(R)::value;
+        constexpr int rp = (r + 2) % 3;
+        char* kl = k8slot(ic<r>{});
+        char* vprev = vslot(ic<rp>{});
+        // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T
+        f32x16 s[2];
+        __builtin_amdgcn_s_setprio(2);
+        if (!idle) {
+          // opaque per-iteration copies: keep the read addresses from being
+          // precomputed for all three slots outside the loop
+          uint32_t xk = kx8, xv = vx, kro = krow8, vro = vrow;
+          asm volatile("" : "+v"(xk), "+v"(xv), "+v"(kro), "+v"(vro));
+          const char* kbase = kl + kro;
+          const char* vbase = vprev + vro;
+          constexpr int NK = 8;                // (mb, kk, 16-byte part)
+          constexpr int NR = NK + 4 * DB;
+          auto rd = [&](int j) -> bf16x8 {
+            if (j < NK) {
+              const int mb = j >> 2, kk = (j >> 1) & 1, part = j & 1;
+              return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)((4 * kk + part) * 16)) ^ xk) + mb * 32 * 128));
+            }
             const int c = (j - NK) / DB, db = (j - NK) % DB;
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
-          }
-          if (j + NIF < NR) fr[j + NIF] = rd(j + NIF);
+            return __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
+          };
+          bf16x8 fr[NR];
+#pragma unroll
+          for (int j = 0; j < NIF; ++j) fr[j] = rd(j);
           __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // vector phase of tile t (ring position r): stage the group's next tile,
-    // the softmax of S(t) -> P(t), then wait for the tile the window
-    // publishes
-    auto vec = [&](int t, auto R) {
-      constexpr int r = decltype(R)::value;
-      if (!group_b) stage(min(t + 3, tl), kslot(ic<(r + 3) & 3>{}));
-      else stage(min(t + 2, tl), vslot(ic<(r + 2) & 3>{}));
-      if (!idle) {
-        const int64_t k0 = (int64_t)t * BN;
-        if (k0 + BN > lim_first) {
-          // key 32 mb + 16 (rr / 8) + 8 half + rr % 8 is masked when it is
-          // >= lrel: compare the lane-independent part (an inline constant)
-          // with lrel - 8 half, so no per-element key index is held in a
-          // register across the loop
-          int thr = (int)min(lim - k0, (int64_t)BN) - 8 * half;
-          asm volatile("" : "+v"(thr));
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-              if (32 * mb + 16 * (rr >> 3) + (rr & 7) >= thr) s[mb][rr] = -INFINITY;
-        }
-        const float sl = a.scale_log2;
-        if (t == t0) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
-          m_run = pair_max(mx) * sl;
-        }
-        const float mneg = -m_run;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int mb = c >> 1, rb = 8 * (c & 1);
-          float acc = lc[c];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
-            acc += p;
-            pp[c][e] = (__bf16)p;
+          for (int j = 0; j < NR; ++j) {
+            if (j < NK) {
+              if (j & 1) {                     // both halves of the (mb, kk) fragment read
+                const int mb = j >> 2, kk = (j >> 1) & 1;
+                const i32x8 af = __builtin_bit_cast(
+                    i32x8, __builtin_shufflevector(__builtin_bit_cast(u32x4, fr[j - 1]), __builtin_bit_cast(u32x4, fr[j]),
+                                                   0, 1, 2, 3, 4, 5, 6, 7));
+                s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qh[kk], kk == 0 ? f32x16{} : s[mb],
+                                                                         0, 0, 0, 127, 0, 127);
+                s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, ql[kk], s[mb], 0, 0, 0, 127, 0, 127);
+              }
+            } else {
+              const int c = (j - NK) / DB, db = (j - NK) % DB;
+              o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
+            }
+            if (j + NIF < NR) fr[j + NIF] = rd(j + NIF);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          lc[c] = acc;
         }
+        __builtin_amdgcn_s_setprio(0);
+        // widen tile t+1 (staged one vector phase ago) into its bf16 slot,
+        // which held tile t-2; the matrix group reaches this barrier before
+        // the vector group, so the work fills its wait
+        wait_vm<0>();
+        if (group_b) widen(min(t + 1, tl), fslot(ic<r + 1>{}), vslot(ic<(r + 1) % 3>{}), sc[(r + 1) % 3], (r + 1) % 3);
+        else if ((tid & (GT - 1)) == 0) scl[0][(r + 1) % 3] = sc[(r + 1) % 3];
+        lds_barrier();
+
+        // ---------------- vector phase: next tile two ahead into the free
+        // slot, then the softmax of tile t -> P(t)
+        sc[(r + 2) % 3] = stage8(min(t + 2, tl), fslot(ic<r + 2>{}));
+        if (!idle) {
+          const int64_t k0 = (int64_t)t * BN;
+          if (k0 + BN > lim_first) {
+            int thr = (int)min(lim - k0, (int64_t)BN) - 8 * half;
+            asm volatile("" : "+v"(thr));
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr)
+                if (32 * mb + 16 * (rr >> 3) + (rr & 7) >= thr) s[mb][rr] = -INFINITY;
+          }
+          // the K scale of tile t multiplies its logits; its V scale
+          // multiplies P(t) (folded into the exponent), the row sum is
+          // divided by it back
+          const float sl = a.scale_log2 * scl[0][r] * qs;
+          if (t == t0) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+            m_run = pair_max(mx) * sl;
+          }
+          const float mneg = __builtin_amdgcn_logf(scl[1][r]) - m_run;
+          float part[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int mb = c >> 1, rb = 8 * (c & 1);
+            float acc = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
+              acc += p;
+              pp[c][e] = (__bf16)p;
+            }
+            part[c] = acc;
+          }
+          // the tile's own V scale divides its sum back out
+          float tsum = (part[0] + part[1]) + (part[2] + part[3]);
+          tsum *= __builtin_amdgcn_rcpf(scl[1][r]);
+          overflow |= !(tsum <= kSlowSum);
+          l_run += tsum;
+        }
+        lds_barrier();
+      };
+
+      int t = t0;
+      for (; t + 2 <= tl; t += 3) {
+        iter(t, ic<0>{});
+        iter(t + 1, ic<1>{});
+        iter(t + 2, ic<2>{});
       }
-      wait_vm<NL>();
-      if (group_b) zero_tail(min(t + 1, tl), vslot(ic<(r + 1) & 3>{}));
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // window k at ring position R = (k - t0) % 4; each group runs its own
-    // loop, with the same number of barriers
-    auto window_a = [&](int k, auto R) {
-      constexpr int r = decltype(R)::value;
-      vec(k, ic<r>{});
-      if (k < tl) mat(k + 1, ic<(r + 1) & 3>{});
-      lds_barrier();
-    };
-    auto window_b = [&](int k, auto R) {
-      constexpr int r = decltype(R)::value;
-      mat(k, ic<r>{});
-      vec(k, ic<r>{});
-      lds_barrier();
-    };
-    int t = t0;
-    if (!group_b) {
-      mat(t0, ic<0>{});                    // the window before t0: group B waits
-      lds_barrier();
-      for (; t + 3 <= tl; t += 4) {
-        window_a(t, ic<0>{});
-        window_a(t + 1, ic<1>{});
-        window_a(t + 2, ic<2>{});
-        window_a(t + 3, ic<3>{});
-      }
-      if (t <= tl) window_a(t, ic<0>{});
-      if (t + 1 <= tl) window_a(t + 1, ic<1>{});
-      if (t + 2 <= tl) window_a(t + 2, ic<2>{});
+      if (t <= tl) iter(t, ic<0>{});
+      if (t + 1 <= tl) iter(t + 1, ic<1>{});
+      final_pv(pp, (tl - t0) % 3);
+      if (tid == 0) item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
+      if (!group_b) lds_barrier();           // balance group B's extra barrier
+
     } else {
-      lds_barrier();
-      for (; t + 3 <= tl; t += 4) {
-        window_b(t, ic<0>{});
-        window_b(t + 1, ic<1>{});
-        window_b(t + 2, ic<2>{});
-        window_b(t + 3, ic<3>{});
+      // bf16: four-slot rings, tile t in slot (t - t0) % 4, one barrier per
+      // tile.  Between two barriers (window k) group A runs the vector phase
+      // of tile k and then the matrix phase of tile k+1, group B the matrix
+      // phase of tile k and then the vector phase of tile k, so the groups are
+      // in opposite phases without a barrier between the phases.  In window k
+      // group A stages K(k+3) and waits for K(k+2), group B stages V(k+2) and
+      // waits for V(k+1) (and clears its tail); the barrier ending the window
+      // publishes both.  The tiles read in window k are K(k), K(k+1), V(k-1)
+      // and V(k), none of them in a slot being staged into.
+      // prologue: K(t0..t0+2) into K slots 0..2 (group A); V(t0), V(t0+1) into
+      // V slots 0, 1 and zeros into V slot 3, which stands for V(t0-1) (group
+      // B); K(t0), K(t0+1) and V(t0) complete before the first barrier.
+      if (!group_b) {
+        stage(t0, lk0);
+        stage(min(t0 + 1, tl), lk1);
+        stage(min(t0 + 2, tl), lk2);
+        wait_vm<NL>();
+      } else {
+        stage(t0, lv0);
+        stage(min(t0 + 1, tl), lv1);
+        const int gt = tid & (GT - 1);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4*>(lv3 + (i * GT + gt) * 16) = u32x4{0, 0, 0, 0};
+        wait_vm<NL>();
+        zero_tail(t0, lv0);
       }
-      if (t <= tl) window_b(t, ic<0>{});
-      if (t + 1 <= tl) window_b(t + 1, ic<1>{});
-      if (t + 2 <= tl) window_b(t + 2, ic<2>{});
-    }
-    final_pv(pp, (tl - t0) & 3);
-    if (tid == 0) item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
+      lds_barrier();
+
+      f32x16 s[2];
+      // matrix phase of tile t (ring position r): S(t) = K(t) Q^T, then
+      // O += V(t-1)^T P(t-1)^T
+      auto mat = [&](int t, auto R) {
+        constexpr int r = decltype(R)::value;
+        char* kl = kslot(ic<r>{});
+        char* vprev = vslot(ic<(r + 3) & 3>{});
+        __builtin_amdgcn_s_setprio(2);
+        if (!idle) {
+          // opaque per-phase copies: keep the read addresses from being
+          // precomputed for all four slots outside the loop
+          uint32_t xk = kx, xv = vx, kro = krow, vro = vrow;
+          asm volatile("" : "+v"(xk), "+v"(xv), "+v"(kro), "+v"(vro));
+          const char* kbase = kl + kro;
+          const char* vbase = vprev + vro;
+          constexpr int NK = 2 * KK;
+          constexpr int NR = NK + 4 * DB;
+          auto rd = [&](int j) -> bf16x8 {
+            if (j < NK) {
+              const int kk = j >> 1, mb = j & 1;
+              return __builtin_bit_cast(bf16x8, ld16(kbase + (((uint32_t)(32 * kk)) ^ xk) + mb * 32 * D * 2));
+            }
+            const int c = (j - NK) / DB, db = (j - NK) % DB;
+            return __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
+          };
+          bf16x8 fr[NR];
+#pragma unroll
+          for (int j = 0; j < NIF; ++j) fr[j] = rd(j);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < NR; ++j) {
+            if (j < NK) {
+              const int kk = j >> 1, mb = j & 1;
+              s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[kk], kk == 0 ? f32x16{} : s[mb], 0, 0, 0);
+            } else {
+              const int c = (j - NK) / DB, db = (j - NK) % DB;
+              o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
+            }
+            if (j + NIF < NR) fr[j + NIF] = rd(j + NIF);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // vector phase of tile t (ring position r): stage the group's next tile,
+      // the softmax of S(t) -> P(t), then wait for the tile the window
+      // publishes
+      auto vec = [&](int t, auto R) {
+        constexpr int r = decltype(R)::value;
+        if (!group_b) stage(min(t + 3, tl), kslot(ic<(r + 3) & 3>{}));
+        else stage(min(t + 2, tl), vslot(ic<(r + 2) & 3>{}));
+        if (!idle) {
+          const int64_t k0 = (int64_t)t * BN;
+          if (k0 + BN > lim_first) {
+            // key 32 mb + 16 (rr / 8) + 8 half + rr % 8 is masked when it is
+            // >= lrel: compare the lane-independent part (an inline constant)
+            // with lrel - 8 half, so no per-element key index is held in a
+            // register across the loop
+            int thr = (int)min(lim - k0, (int64_t)BN) - 8 * half;
+            asm volatile("" : "+v"(thr));
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr)
+                if (32 * mb + 16 * (rr >> 3) + (rr & 7) >= thr) s[mb][rr] = -INFINITY;
+          }
+          const float sl = a.scale_log2;
+          if (t == t0) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+            m_run = pair_max(mx) * sl;
+          }
+          const float mneg = -m_run;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int mb = c >> 1, rb = 8 * (c & 1);
+            float acc = lc[c];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][rb + e], sl, mneg));
+              acc += p;
+              pp[c][e] = (__bf16)p;
+            }
+            lc[c] = acc;
+          }
+        }
+        wait_vm<NL>();
+        if (group_b) zero_tail(min(t + 1, tl), vslot(ic<(r + 1) & 3>{}));
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // window k at ring position R = (k - t0) % 4; each group runs its own
+      // loop, with the same number of barriers
+      auto window_a = [&](int k, auto R) {
+        constexpr int r = decltype(R)::value;
+        vec(k, ic<r>{});
+        if (k < tl) mat(k + 1, ic<(r + 1) & 3>{});
+        lds_barrier();
+      };
+      auto window_b = [&](int k, auto R) {
+        constexpr int r = decltype(R)::value;
+        mat(k, ic<r>{});
+        vec(k, ic<r>{});
+        lds_barrier();
+      };
+      int t = t0;
+      if (!group_b) {
+        mat(t0, ic<0>{});                    // the window before t0: group B waits
+        lds_barrier();
+        for (; t + 3 <= tl; t += 4) {
+          window_a(t, ic<0>{});
+          window_a(t + 1, ic<1>{});
+          window_a(t + 2, ic<2>{});
+          window_a(t + 3, ic<3>{});
+        }
+        if (t <= tl) window_a(t, ic<0>{});
+        if (t + 1 <= tl) window_a(t + 1, ic<1>{});
+        if (t + 2 <= tl) window_a(t + 2, ic<2>{});
+      } else {
+        lds_barrier();
+        for (; t + 3 <= tl; t += 4) {
+          window_b(t, ic<0>{});
+          window_b(t + 1, ic<1>{});
+          window_b(t + 2, ic<2>{});
+          window_b(t + 3, ic<3>{});
+        }
+        if (t <= tl) window_b(t, ic<0>{});
+        if (t + 1 <= tl) window_b(t + 1, ic<1>{});
+        if (t + 2 <= tl) window_b(t + 2, ic<2>{});
+      }
+      final_pv(pp, (tl - t0) & 3);
+      if (tid == 0) item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
     }
     wait_vm<0>();                          // no direct load outlives the item
   } else if (tid == 0) {
