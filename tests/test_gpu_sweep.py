@@ -1,13 +1,17 @@
-"""Seeded sweep of block_causal_attn over call shapes drawn at random against
-the oracle: 1-3 heads, head dims 64 and 128, page sizes 16-256 with shuffled
-page tables, key counts from 1 to 5000 (so every remainder of key tiles per
-split and per unrolled loop body turns up), query counts and positions,
-block sizes from causal (1) to all-visible, with and without a workspace;
-bf16 caches, and fp8 caches (head dim 128, pages of 64+ keys).  The shapes
-come from fixed seeds, so every run checks the same cases.  Bars as in the
-other attention tests: bf16 max-abs 2e-2 and relative RMS 1e-2, fp8 max-abs
-3e-2 and relative RMS 1e-2, against the oracle's dense-mask attention over
-the keys as the cache holds them."""
+"""Seeded sweeps against the oracle over shapes drawn at random (fixed
+seeds, so every run checks the same cases).
+
+block_causal_attn: 1-3 heads, head dims 64 and 128, page sizes 16-256 with
+shuffled page tables, key counts from 1 to 5000 (so every remainder of key
+tiles per split and per unrolled loop body turns up), query counts and
+positions, block sizes from causal (1) to all-visible, with and without a
+workspace; bf16 caches, and fp8 caches (head dim 128, pages of 64+ keys).
+Bars as in the other attention tests: bf16 max-abs 2e-2 and relative RMS
+1e-2, fp8 max-abs 3e-2 and relative RMS 1e-2, against the oracle's
+dense-mask attention over the keys as the cache holds them.
+
+kv_append: random sequences of appends into bf16, fp32 and fp8 caches, bit
+for bit."""
 import numpy as np
 import pytest
 import torch
@@ -66,3 +70,54 @@ def test_sweep_bf16(i):
 @pytest.mark.parametrize("i", range(N_FP8))
 def test_sweep_fp8(i):
     _run(i, True)
+
+
+N_APPEND = 24
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).cpu().numpy()
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("i", range(N_APPEND))
+def test_sweep_append(i):
+    """Random sequences of 1-6 appends (1-600 tokens each, any start within a
+    page) into bf16, fp32 and fp8 caches with shuffled page tables: after
+    each append every page equals the oracle's bit for bit (fp8: the codes
+    and scales of every page written so far, partly filled pages being
+    re-quantised by later appends; the values' scale changes from append to
+    append so the scales grow and shrink)."""
+    r = np.random.default_rng(8000 + i)
+    dt = str(r.choice(["bf16", "f32", "fp8"]))
+    H = int(r.integers(1, 5))
+    D = 128 if dt == "fp8" else int(r.choice([64, 128] if dt == "bf16" else [32, 64]))
+    ps = int(r.choice([64, 128, 256] if dt == "fp8" else [16, 32, 64, 256]))
+    sizes = [int(x) for x in r.integers(1, 601, size=int(r.integers(1, 7)))]
+    shuffle = int(r.integers(1, 1000))
+    say(f"sweep append case {i}: {dt} H={H} D={D} ps={ps} sizes={sizes}")
+    g, o, _ = make_caches(bca, H, D, ps, dt, sum(sizes), shuffle)
+    for j, n in enumerate(sizes):
+        sc = float(r.choice([0.05, 0.5, 3.0]))
+        src = "f32" if dt == "f32" else "bf16"
+        k = workloads.qkv(20000 + 100 * i + j, n, H, D, sc, src)
+        v = workloads.qkv(30000 + 100 * i + j, n, H, D, sc, src)
+        bca.kv_append(g, k.cuda(), v.cuda())
+        o.append(k.double().numpy() if dt != "fp8" else k.float().numpy(),
+                 v.double().numpy() if dt != "fp8" else v.float().numpy())
+        assert g.n_tokens == o.n_tokens
+        torch.cuda.synchronize()
+        if dt == "fp8":
+            pages = g.page_table.cpu().numpy()[: -(-o.n_tokens // ps)]
+            np.testing.assert_array_equal(g.k_pages.cpu().numpy()[pages], o.k_codes[pages])
+            np.testing.assert_array_equal(g.v_pages.cpu().numpy()[pages], o.v_codes[pages])
+            np.testing.assert_array_equal(g.k_scales.cpu().numpy()[pages], o.k_scales[pages])
+            np.testing.assert_array_equal(g.v_scales.cpu().numpy()[pages], o.v_scales[pages])
+        else:
+            want_k = torch.from_numpy(o.k_pages).to(torch.bfloat16 if dt == "bf16" else torch.float32)
+            want_v = torch.from_numpy(o.v_pages).to(torch.bfloat16 if dt == "bf16" else torch.float32)
+            np.testing.assert_array_equal(_bits(g.k_pages), _bits(want_k))
+            np.testing.assert_array_equal(_bits(g.v_pages), _bits(want_v))
