@@ -11,14 +11,14 @@ Bars as in the other attention tests: bf16 max-abs 2e-2 and relative RMS
 dense-mask attention over the keys as the cache holds them.
 
 kv_append: random sequences of appends into bf16, fp32 and fp8 caches, bit
-for bit."""
+for bit.  performer_unit: random unit, history, step and channel counts."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from _helpers import assert_close, make_caches, np64, say
+from _helpers import assert_close, assert_latents, make_caches, np64, say
 
 pytestmark = pytest.mark.gpu
 bca = pytest.importorskip("block_causal_attention_performer_amd")
@@ -121,3 +121,55 @@ def test_sweep_append(i):
             want_v = torch.from_numpy(o.v_pages).to(torch.bfloat16 if dt == "bf16" else torch.float32)
             np.testing.assert_array_equal(_bits(g.k_pages), _bits(want_k))
             np.testing.assert_array_equal(_bits(g.v_pages), _bits(want_v))
+
+
+N_UNIT = 16
+
+
+@pytest.mark.parametrize("i", range(N_UNIT))
+def test_sweep_performer_unit(i):
+    """performer_unit on random shapes: 1-4 heads, unit lengths 1-200, a
+    history of 0-3000 tokens (rarely a multiple of the unit), 1-6 solver
+    steps, 3-16 latent channels, page sizes 16-256, with and without a
+    workspace; bf16, fp32 and fp8 caches.  O and z (and the solver's move
+    z - eps) against the oracle's performer unit on all rows."""
+    r = np.random.default_rng(8500 + i)
+    dt = str(r.choice(["bf16", "f32", "fp8"]))
+    H = int(r.integers(1, 5))
+    D = 128 if dt == "fp8" else int(r.choice([64, 128]))
+    ps = int(r.choice([64, 256] if dt == "fp8" else [16, 64, 256]))
+    lq = int(r.integers(1, 201))
+    n_hist = int(r.integers(0, 3001))
+    S = int(r.integers(1, 7))
+    C = int(r.choice([3, 8, 16]))
+    with_ws = bool(r.integers(0, 2))
+    shuffle = int(r.integers(1, 1000))
+    say(f"sweep unit case {i}: {dt} H={H} D={D} ps={ps} lq={lq} hist={n_hist} S={S} C={C} ws={with_ws}")
+    cap = n_hist + lq
+    g, o, _ = make_caches(bca, H, D, ps, dt, cap, shuffle)
+    src = "f32" if dt == "f32" else "bf16"
+    seed = 40000 + 10 * i
+    q = workloads.qkv(seed, lq, H, D, 0.5, src)
+    kh = workloads.qkv(seed + 1, n_hist, H, D, 0.5, src)
+    vh = workloads.qkv(seed + 2, n_hist, H, D, 0.5, src)
+    kn = workloads.qkv(seed + 3, lq, H, D, 0.5, src)
+    vn = workloads.qkv(seed + 4, lq, H, D, 0.5, src)
+    eps = workloads.randn((lq, C), seed + 5)
+    w = workloads.randn((H * D, C), seed + 6)
+    if n_hist:
+        bca.kv_append(g, kh.cuda(), vh.cuda())
+        o.append(kh.double().numpy(), vh.double().numpy())
+    z = eps.clone().cuda()
+    ws = bca.alloc_workspace(bca.workspace_bytes(g, lq, cap, C)) if with_ws else None
+    osc = torch.empty((lq, H, D), dtype=g.compute_dtype, device="cuda")
+    bca.performer_unit(g, kn.cuda(), vn.cuda(), q.cuda(), w.cuda(), z, S, o_scratch=osc, workspace=ws)
+    zw, ow = oracle.performer_unit(o, kn.double().numpy(), vn.double().numpy(), q.double().numpy(),
+                                   w.double().numpy(), eps.double().numpy(), S)
+    e = eps.double().numpy()
+    if dt == "f32":
+        assert_close(np64(osc), ow, 1e-4, what=f"unit case {i} O")
+        assert_latents(np64(z), zw, e, 1e-4, 1e-4, what=f"unit case {i}")
+    else:
+        tol = 3e-2 if dt == "fp8" else 2e-2
+        assert_close(np64(osc), ow, tol, 1e-2, what=f"unit case {i} O")
+        assert_latents(np64(z), zw, e, tol, 1e-2, what=f"unit case {i}")
