@@ -11,7 +11,8 @@ Bars as in the other attention tests: bf16 max-abs 2e-2 and relative RMS
 dense-mask attention over the keys as the cache holds them.
 
 kv_append: random sequences of appends into bf16, fp32 and fp8 caches, bit
-for bit.  performer_unit: random unit, history, step and channel counts."""
+for bit.  performer_unit: random unit, history, step and channel counts.
+Streaming sessions: random unit lengths, page sizes, dtypes, graph or eager."""
 import numpy as np
 import pytest
 import torch
@@ -173,3 +174,56 @@ def test_sweep_performer_unit(i):
         tol = 3e-2 if dt == "fp8" else 2e-2
         assert_close(np64(osc), ow, tol, 1e-2, what=f"unit case {i} O")
         assert_latents(np64(z), zw, e, tol, 1e-2, what=f"unit case {i}")
+
+
+N_SESSION = 8
+
+
+@pytest.mark.parametrize("i", range(N_SESSION))
+def test_sweep_session(i):
+    """Streaming sessions on random shapes: 3-6 units of random and varying
+    lengths (1-300 tokens, so units start anywhere inside pages), pages of
+    16-256 tokens taken from a shuffled free list, bf16 or fp8 caches, 1-4
+    solver steps, eager or replayed as HIP graphs.  Each unit's O and z
+    against the oracle's performer unit over a cache with the same logical
+    contents; the free-page count and the page table at the end."""
+    r = np.random.default_rng(8800 + i)
+    dt = str(r.choice(["bf16", "fp8"]))
+    H = int(r.integers(1, 4))
+    D = 128
+    ps = int(r.choice([64, 256] if dt == "fp8" else [16, 64, 256]))
+    lens = [int(x) for x in r.integers(1, 301, size=int(r.integers(3, 7)))]
+    S = int(r.integers(1, 5))
+    C = int(r.choice([8, 16]))
+    use_graph = bool(r.integers(0, 2))
+    total = sum(lens)
+    n_phys = -(-total // ps) + 2
+    free = [int(x) for x in r.permutation(n_phys)]
+    say(f"sweep session case {i}: {dt} H={H} ps={ps} lens={lens} S={S} C={C} graph={use_graph}")
+    pt = torch.full((n_phys,), -1, dtype=torch.int32)
+    g = bca.KVCache(H, D, ps, pt, n_phys, dt)
+    ss = bca.Session(g, free)
+    ref = (oracle.PagedCacheFP8 if dt == "fp8" else oracle.PagedCache)(H, D, ps, free, n_phys)
+    w = workloads.randn((H * D, C), 50000 + i)
+    ws = bca.alloc_workspace(bca.workspace_bytes(g, max(lens), total, C))
+    tol = 3e-2 if dt == "fp8" else 2e-2
+    for u, n in enumerate(lens):
+        seed = 51000 + 100 * i + 10 * u
+        k = workloads.qkv(seed, n, H, D, 0.5, "bf16")
+        v = workloads.qkv(seed + 1, n, H, D, 0.5, "bf16")
+        q = workloads.qkv(seed + 2, n, H, D, 0.5, "bf16")
+        eps = workloads.randn((n, C), seed + 3)
+        z = eps.clone().cuda()
+        osc = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+        ss.unit(k.cuda(), v.cuda(), q.cuda(), w.cuda(), z, S, osc, workspace=ws, use_graph=use_graph)
+        torch.cuda.synchronize()
+        z_want, o_want = oracle.performer_unit(ref, k.double().numpy(), v.double().numpy(),
+                                               q.double().numpy(), w.double().numpy(),
+                                               eps.double().numpy(), S)
+        assert_close(np64(osc), o_want, tol, 1e-2, what=f"session case {i} unit {u} O")
+        assert_latents(np64(z), z_want, eps.double().numpy(), tol, 1e-2, what=f"session case {i} unit {u}")
+    used = -(-total // ps)
+    assert ss.free_pages == n_phys - used
+    assert g.page_table[:used].cpu().tolist() == free[:used]
+    assert g.n_tokens == total
+    ss.close()
