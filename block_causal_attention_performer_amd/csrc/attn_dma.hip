@@ -24,7 +24,9 @@
 // only).  bf16 pages: rings of four slots and one barrier per key tile (a
 // barrier between the two phases cost more in waiting than the skew it
 // removed); fp8 pages: rings of three slots, a barrier after each phase,
-// and V^T widened to bf16 in LDS between them.
+// and V^T widened to bf16 in LDS by group B between the MFMAs of its matrix
+// phase, where the conversions take issue slots the MFMA chains leave free
+// (at the end of the phase they lengthened it by ~7%).
 //
 // The loads use the buffer (MUBUF) form with a per-tile descriptor, not the
 // global (FLAT-encoded) form: the compiler treats a FLAT direct load in
@@ -58,6 +60,10 @@ constexpr int NT = NW * 64;
 constexpr int GT = NT / 2;        // threads per group
 constexpr int BM = NW * QW;       // query rows per workgroup
 constexpr int NIF = 4;            // LDS reads kept in flight ahead of the MFMAs
+// fp8 matrix phase: the step at which group B's V^T widening starts, and
+// the steps between its parts (0/2, 1/3, 1/6, 3/2 and 5/4 timed within 1%)
+constexpr int kWidenAt = 1;
+constexpr int kWidenStep = 3;
 static_assert(NW == kAttnFlagWaves, "one overflow flag per wave");
 
 template <int N>
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   // group B
   constexpr int SLOT8 = FP8 ? BN * D : 16;   // bytes per fp8 K or V^T slot
   constexpr int NL8 = FP8 ? SLOT8 / (GT * 16) : 1;
+  static_assert(!FP8 || NL8 == 2, "the fp8 widening runs in two parts");
 
   // bf16: four-slot K and V^T rings; fp8: three-slot bf16 V^T ring (K is
   // read from the fp8 ring), so its fourth slots and the bf16 K slots are
@@ -362,17 +369,12 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
   };
   // fp8, group B: widen the V^T chunks this thread loaded (fp8 slot `src`)
   // into the swizzled bf16 slot `dst` (exact: E4M3 fits bf16), zeroing the
-  // entries of keys >= n_kv, and publish the tile's scale in scl[1][ss].
+  // entries of keys >= n_kv, and publish the tile's V scale sc in scl[1][ss].
   // Chunk q = head-dim row q / 4, keys (q % 4) * 16 .. +15 -> bf16 chunks
   // 2 (q % 4) and + 1 of that row.
-  auto widen = [&](int t, const char* src, char* dst, float sc, int ss) {
-    const int gt = tid & (GT - 1);
-    const int64_t k0 = (int64_t)t * BN;
-    const int nvalid = (int)min((int64_t)BN, a.n_kv - k0);
-#pragma unroll
-    for (int i = 0; i < NL8; ++i) {
-      const int q = i * GT + gt;
-      const u32x4 c = *reinterpret_cast<const u32x4*>(src + q * 16);
+  auto widen_one = [&](int i, const u32x4 c, int nvalid, char* dst, auto Masked) {
+    const int q = i * GT + (tid & (GT - 1));
+    {
       u32x4 lo, hi;
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
         hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w + 2], 1.0f, true));
       }
       const int d = q >> 2, cq = q & 3;
-      if (nvalid < BN) {
+      if (decltype(Masked)::value && nvalid < BN) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int key = 16 * cq + 2 * w;
@@ -396,7 +398,17 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       *reinterpret_cast<u32x4*>(rp + (((2 * cq) ^ swz<8>(d)) * 16)) = lo;
       *reinterpret_cast<u32x4*>(rp + (((2 * cq + 1) ^ swz<8>(d)) * 16)) = hi;
     }
-    if (gt == 0) scl[1][ss] = sc;
+  };
+  auto nvalid_of = [&](int t) { return (int)min((int64_t)BN, a.n_kv - (int64_t)t * BN); };
+  auto widen_tile = [&](int t, const char* src, char* dst) {
+    const int gt = tid & (GT - 1);
+    const int nvalid = nvalid_of(t);
+#pragma unroll
+    for (int i = 0; i < NL8; ++i) widen_one(i, ld16(src + (i * GT + gt) * 16), nvalid, dst, ic<1>{});
+  };
+  auto widen = [&](int t, const char* src, char* dst, float sc, int ss) {
+    widen_tile(t, src, dst);
+    if ((tid & (GT - 1)) == 0) scl[1][ss] = sc;
   };
 
   // O += V(last)^T P(last)^T, V(last) in V slot rl
@@ -453,13 +465,22 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
       lds_barrier();
       if (group_b) lds_barrier();            // group B runs one phase behind
 
-      auto iter = [&](int t, auto R) {
+      // G: the group (0 = A, 1 = B), fixed per loop so that group B's
+      // widening steps sit between its MFMAs without a branch
+      auto iter = [&](int t, auto R, auto G) {
         constexpr int r = decltype(R)::value;
+        constexpr bool GB = decltype(G)::value != 0;
         constexpr int rp = (r + 2) % 3;
         char* kl = k8slot(ic<r>{});
         char* vprev = vslot(ic<rp>{});
         // ---------------- matrix phase: S(t), then O += V(t-1)^T P(t-1)^T
         f32x16 s[2];
+        // group B widens V(t+1), staged one phase ago, into the bf16 slot that
+        // held V(t-2), between its MFMAs
+        const int wt = min(t + 1, tl);
+        const char* wsrc = fslot(ic<r + 1>{});
+        char* wdst = vslot(ic<(r + 1) % 3>{});
+        const int wgt = tid & (GT - 1);
         __builtin_amdgcn_s_setprio(2);
         if (!idle) {
           // opaque per-iteration copies: keep the read addresses from being
@@ -479,6 +500,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
             return __builtin_bit_cast(bf16x8, ld16(vbase + (((uint32_t)(32 * c)) ^ xv) + db * 32 * BN * 2));
           };
           bf16x8 fr[NR];
+          u32x4 wc;
 #pragma unroll
           for (int j = 0; j < NIF; ++j) fr[j] = rd(j);
           __builtin_amdgcn_sched_barrier(0);
@@ -499,16 +521,32 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
               o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pp[c], o[db], 0, 0, 0);
             }
             if (j + NIF < NR) fr[j + NIF] = rd(j + NIF);
+            if constexpr (GB) {
+              // the conversions fill the issue slots the MFMA chains leave
+              // (without the tail mask, which would put a branch among the
+              // MFMAs: the one tile that ends past n_kv is widened again,
+              // masked, before the last PV step)
+              if (j == kWidenAt) {
+                wait_vm<0>();
+                wc = ld16(wsrc + wgt * 16);
+              } else if (j == kWidenAt + kWidenStep) {
+                widen_one(0, wc, 0, wdst, ic<0>{});
+                wc = ld16(wsrc + (GT + wgt) * 16);
+              } else if (j == kWidenAt + 2 * kWidenStep) {
+                widen_one(1, wc, 0, wdst, ic<0>{});
+              }
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
         }
         __builtin_amdgcn_s_setprio(0);
-        // widen tile t+1 (staged one vector phase ago) into its bf16 slot,
-        // which held tile t-2; the matrix group reaches this barrier before
-        // the vector group, so the work fills its wait
         wait_vm<0>();
-        if (group_b) widen(min(t + 1, tl), fslot(ic<r + 1>{}), vslot(ic<(r + 1) % 3>{}), sc[(r + 1) % 3], (r + 1) % 3);
-        else if ((tid & (GT - 1)) == 0) scl[0][(r + 1) % 3] = sc[(r + 1) % 3];
+        if (group_b) {
+          if (idle) widen(wt, wsrc, wdst, sc[(r + 1) % 3], (r + 1) % 3);
+          else if (wgt == 0) scl[1][(r + 1) % 3] = sc[(r + 1) % 3];
+        } else if (wgt == 0) {
+          scl[0][(r + 1) % 3] = sc[(r + 1) % 3];
+        }
         lds_barrier();
 
         // ---------------- vector phase: next tile two ahead into the free
@@ -560,14 +598,32 @@ __global__ __launch_bounds__(NT, 1) void attn_dma_kernel(AttnArgs a) {
         lds_barrier();
       };
 
-      int t = t0;
-      for (; t + 2 <= tl; t += 3) {
-        iter(t, ic<0>{});
-        iter(t + 1, ic<1>{});
-        iter(t + 2, ic<2>{});
+      auto run = [&](auto G) {
+        int t = t0;
+        for (; t + 2 <= tl; t += 3) {
+          iter(t, ic<0>{}, G);
+          iter(t + 1, ic<1>{}, G);
+          iter(t + 2, ic<2>{}, G);
+        }
+        if (t <= tl) iter(t, ic<0>{}, G);
+        if (t + 1 <= tl) iter(t + 1, ic<1>{}, G);
+      };
+      if (group_b) run(ic<1>{});
+      else run(ic<0>{});
+      if (tl > t0 && nvalid_of(tl) < BN) {
+        // the last tile ends past n_kv: group A widens it again from its
+        // codes with the tail zeroed (the codes are still in its fp8 slot:
+        // the re-stagings of the clamped tiles past tl went to the other two
+        // slots) while group B runs its last vector phase, and the barrier
+        // publishes it before either group's last PV step
+        if (!group_b) {
+          const int rl = (tl - t0) % 3;
+          if (rl == 0) widen_tile(tl, fv0, lv0);
+          else if (rl == 1) widen_tile(tl, fv1, lv1);
+          else widen_tile(tl, fv2, lv2);
+        }
+        lds_barrier();
       }
-      if (t <= tl) iter(t, ic<0>{});
-      if (t + 1 <= tl) iter(t + 1, ic<1>{});
       final_pv(pp, (tl - t0) % 3);
       if (tid == 0) item_sh[nxt] = settle(atomicAdd(a.sched + cur_q, 1));
       if (!group_b) lds_barrier();           // balance group B's extra barrier

@@ -170,6 +170,34 @@ def test_fp8_attention(ws, n_kv, n_q, ps):
     assert_close(np64(out), want, FP8_TOL, FP8_REL, what="fp8 attention")
 
 
+@pytest.mark.parametrize("ws", [False, True])
+@pytest.mark.parametrize("n_kv,n_q", [(2000, 333), (4000, 700), (130, 64)])
+def test_fp8_nan_codes_past_n_kv(ws, n_kv, n_q):
+    """Codes past n_kv in the last page set to 0x7F (an E4M3 NaN) change no
+    output bit: the tile that ends past n_kv has its tail zeroed before any
+    PV step reads it (0 * NaN would be NaN)."""
+    H, D, ps = 3, 128, 256
+    say(f"fp8 NaN codes past n_kv={n_kv} n_q={n_q} ws={ws}")
+    q = workloads.qkv(71, n_q, H, D, 0.5, "bf16").cuda()
+    k = workloads.qkv(72, n_kv, H, D, 0.5, "bf16").cuda()
+    v = workloads.qkv(73, n_kv, H, D, 0.5, "bf16").cuda()
+    outs = []
+    for poison in (False, True):
+        g, _, pt = make_caches(bca, H, D, ps, "fp8", n_kv, 6)
+        bca.kv_append(g, k, v)
+        if poison:
+            last = int(pt[(n_kv - 1) // ps])
+            off = n_kv % ps
+            assert off > 0
+            g.k_pages[last, :, off:, :] = 0x7F
+            g.v_pages[last, :, :, off:] = 0x7F
+        wsb = bca.alloc_workspace(bca.workspace_bytes(g, n_q, n_kv)) if ws else None
+        outs.append(bca.block_causal_attn(q, g, workspace=wsb))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0].float()).all()
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("n_kv,n_q,ps", [(3000, 200, 256), (1000, 300, 64)])
 def test_fp8_attention_sharp_softmax(n_kv, n_q, ps):
     """Logits x4 (Q and K drawn at 2.0, logit std ~4) on the fast path, where
