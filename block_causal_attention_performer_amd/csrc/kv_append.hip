@@ -12,7 +12,8 @@
 namespace bca {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;               // fp8 append kernel
+constexpr int kCopyThreads = 256;           // bf16 / f32 copy kernel
 
 // Transpose an E x E block held as E rows of 16 bytes (row = token,
 // column = head dim) into E rows of head dims, each holding E tokens.
@@ -35,18 +36,22 @@ __device__ __forceinline__ void transpose_block(const u32x4 (&in)[16 / sizeof(T)
   }
 }
 
-// One wave per (TPW consecutive tokens, head), over the tokens [g0, g1) of
-// the slice whose E-aligned groups it covers fully.  Lane (to, j) moves the
+// One workgroup of four waves per (TPW consecutive tokens, head), over the
+// tokens [g0, g1) of the slice whose E-aligned groups it covers fully (four
+// waves rather than one: a workgroup's V^T stores then cover 256 bytes of
+// each head-dim row, so a slice that starts off a 64-byte boundary writes
+// fewer partial lines; 38 against 44 us for the v0.2 slice at such a
+// start, the same 32 us at an aligned one).  Thread (to, j) moves the
 // E tokens t0 = g0 + to*E .. +E-1, head dims j*E .. +E-1: E 16-byte loads of
 // K and of V; K rows are stored as they are, the V block is transposed in
 // registers and stored as E runs of E tokens of the V^T rows.  The E tokens
 // lie in one page (pages hold >= 16 tokens, groups are E-aligned).
 // T: element type (uint16_t for bf16, float for f32); D: head dim.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void append_copy_kernel(AppendArgs a, int64_t g0, int64_t g1) {
+__global__ __launch_bounds__(kCopyThreads) void append_copy_kernel(AppendArgs a, int64_t g0, int64_t g1) {
   constexpr int E = 16 / sizeof(T);          // elements per 16-byte vector
   constexpr int JO = D / E;                  // 16-byte chunks per token row
-  constexpr int TO = 64 / JO;                // token groups per wave
+  constexpr int TO = kCopyThreads / JO;      // token groups per workgroup
   constexpr int TPW = TO * E;                // tokens per workgroup
   const int lane = threadIdx.x;
   const int j = lane % JO, to = lane / JO;
@@ -236,12 +241,12 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(AppendArgs a) {
 template <typename T, int D>
 hipError_t launch_copy_t(const AppendArgs& a, hipStream_t s) {
   constexpr int E = 16 / (int)sizeof(T);
-  constexpr int TPW = 64 / (D / E) * E;
+  constexpr int TPW = kCopyThreads / (D / E) * E;
   const int64_t lo = a.n0, hi = a.n0 + a.n_new;
   const int64_t g0 = (lo + E - 1) / E * E, g1 = hi / E * E;
   if (g1 > g0) {
     dim3 grid((unsigned)((g1 - g0 + TPW - 1) / TPW), (unsigned)a.n_heads);
-    append_copy_kernel<T, D><<<grid, 64, 0, s>>>(a, g0, g1);
+    append_copy_kernel<T, D><<<grid, kCopyThreads, 0, s>>>(a, g0, g1);
   }
   const int64_t n_edge = g1 > g0 ? (g0 - lo) + (hi - g1) : a.n_new;
   if (n_edge > 0) {
