@@ -31,7 +31,9 @@
  *     host-side: a 16-entry memo of the attention split count per call
  *     shape (behind a mutex, so calls from several threads are safe; it
  *     changes no result, only which split count a shape gets without
- *     re-running the model that picks it).  The streaming session
+ *     re-running the model that picks it); performer_unit_noalloc alone
+ *     adds a fixed per-GPU device array and its looked-up address (see its
+ *     declaration).  The streaming session
  *     (bca_session_*) is the one object the library creates: host
  *     bookkeeping plus the HIP graphs it replays, owned by the caller
  *     through the session handle.
